@@ -1,0 +1,141 @@
+"""The page / tile plan, written out rule by rule (test infrastructure only).
+
+KPage abstract, sentence 2: keys and values are cut into 16-row pages of valid tokens,
+and pages are packed across logical-block boundaries into large tiles while loading.
+Sentence 3: Q blocks are routed between 64x256 and 128x128 tiles to cut query-side
+padding.  Sentence 4: each page is owned by one K/V block ("K/V-owned"), so exact
+masking keeps the sparse graph.  Sentence 7: physical query-key pair capacity (what the
+tiles hold, padding included) versus useful pairs (the graph's edges).
+
+Readings of what the abstract leaves open (one per rule):
+  R1 selection   a (unit, Q block) row selects a *set* of K blocks: sorted, deduplicated;
+                 ids must be in range.
+  R2 pages       a K block of n >= 1 slots has pages p = 0 .. ceil(n/16)-1, page p covering
+                 slots [16p, min(16p+16, n)) of that block; an empty block has no pages.
+  R3 tile shapes (Q rows x K columns) = 128x128 (8 pages per K tile) or 64x256 (16 pages).
+  R4 Q routing   a Q block of n >= 1 rows gives floor(n/128) 128-row tiles in row order, then
+                 for r = n mod 128: one 64-row tile if 0 < r <= 64, one 128-row tile if r > 64.
+  R5 K tiles     a Q tile's page sequence is the pages of its selected blocks, block ascending
+                 then page ascending, cut into ceil(n_pages / pages_per_tile) K tiles; only
+                 the last K tile may hold empty page slots.  Nothing is pruned for causality.
+  R6 counts      useful U = pairs in the graph (causal exclusions removed); physical
+                 P = sum over (batch, head) and Q tiles of tile_rows * tile_cols * n_ktiles.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional
+
+import numpy as np
+
+from .attention import selected_blocks, selection_unit, useful_pairs
+
+PAGE = 16
+SHAPE_128x128 = 0
+SHAPE_64x256 = 1
+TILE_ROWS = {SHAPE_128x128: 128, SHAPE_64x256: 64}
+TILE_COLS = {SHAPE_128x128: 128, SHAPE_64x256: 256}
+PAGES_PER_KTILE = {SHAPE_128x128: 8, SHAPE_64x256: 16}
+
+
+@dataclasses.dataclass
+class Plan:
+    # K pages (R2), in K-block order then page order; a page id is an index here
+    page_kblock: np.ndarray
+    page_slot0: np.ndarray      # absolute slot of the page's first row in the K layout
+    page_nvalid: np.ndarray     # 1..16
+    # Q tiles (R4), in Q-block order then row order
+    qt_qblock: np.ndarray
+    qt_row0: np.ndarray         # absolute slot of the tile's first row in the Q layout
+    qt_rows: np.ndarray         # valid rows, 1..128 (or 1..64 for a 64-row tile)
+    qt_shape: np.ndarray        # SHAPE_128x128 or SHAPE_64x256
+    # page lists (R5) per (unit, Q block) row, CSR
+    n_units: int
+    pl_ptr: np.ndarray          # int64 [n_units * n_qblocks + 1]
+    pl_pages: np.ndarray        # int32 page ids
+    # counts (R6), over all (batch, head)
+    useful: int
+    physical: int
+    n_ktiles: int
+
+    @property
+    def n_pages(self) -> int:
+        return int(self.page_kblock.shape[0])
+
+    @property
+    def n_qtiles128(self) -> int:
+        return int(np.sum(self.qt_shape == SHAPE_128x128))
+
+    @property
+    def n_qtiles64(self) -> int:
+        return int(np.sum(self.qt_shape == SHAPE_64x256))
+
+
+def build_plan(B, Hq, Hkv, q_offsets, q_perm, k_offsets, k_perm, sel_nb, sel_nh, sel_row_ptr, sel_kblk,
+               causal=False, q_pos0=0, page_size=PAGE) -> Plan:
+    if page_size != PAGE:
+        raise ValueError("only 16-row pages are defined")
+    nqb, nkb = len(q_offsets) - 1, len(k_offsets) - 1
+    n_units = sel_nb * sel_nh
+    if len(sel_row_ptr) != n_units * nqb + 1:
+        raise ValueError("selection row_ptr has the wrong length")
+
+    # R2: pages
+    pk, ps, pn = [], [], []
+    first_page = [0]
+    for kb in range(nkb):
+        s0, s1 = int(k_offsets[kb]), int(k_offsets[kb + 1])
+        n = s1 - s0
+        for p in range((n + PAGE - 1) // PAGE):
+            pk.append(kb)
+            ps.append(s0 + PAGE * p)
+            pn.append(min(PAGE, n - PAGE * p))
+        first_page.append(len(pk))
+
+    # R4: Q routing
+    qq, qr, qn, qs = [], [], [], []
+    for qb in range(nqb):
+        s0, s1 = int(q_offsets[qb]), int(q_offsets[qb + 1])
+        n = s1 - s0
+        full, r = divmod(n, 128)
+        for t in range(full):
+            qq.append(qb); qr.append(s0 + 128 * t); qn.append(128); qs.append(SHAPE_128x128)
+        if 0 < r <= 64:
+            qq.append(qb); qr.append(s0 + 128 * full); qn.append(r); qs.append(SHAPE_64x256)
+        elif r > 64:
+            qq.append(qb); qr.append(s0 + 128 * full); qn.append(r); qs.append(SHAPE_128x128)
+
+    # R1 + R5: page lists per (unit, Q block)
+    pl_ptr = [0]
+    pl = []
+    for u in range(n_units):
+        for qb in range(nqb):
+            for kb in selected_blocks(sel_row_ptr, sel_kblk, u * nqb + qb, nkb):
+                pl.extend(range(first_page[kb], first_page[kb + 1]))
+            pl_ptr.append(len(pl))
+    pl_ptr = np.asarray(pl_ptr, dtype=np.int64)
+
+    # R6: physical capacity and K-tile count over every (batch, head)
+    physical = 0
+    nkt = 0
+    for b in range(B):
+        for h in range(Hq):
+            u = selection_unit(b, h, B, Hq, Hkv, sel_nb, sel_nh)
+            for t in range(len(qq)):
+                row = u * nqb + qq[t]
+                npg = int(pl_ptr[row + 1] - pl_ptr[row])
+                kt = -(-npg // PAGES_PER_KTILE[qs[t]])
+                nkt += kt
+                physical += TILE_ROWS[qs[t]] * TILE_COLS[qs[t]] * kt
+    useful = useful_pairs(q_offsets, q_perm, k_offsets, k_perm, B, Hq, Hkv, sel_nb, sel_nh,
+                          sel_row_ptr, sel_kblk, causal, q_pos0)
+    i32 = lambda a: np.asarray(a, dtype=np.int32)  # noqa: E731
+    return Plan(page_kblock=i32(pk), page_slot0=i32(ps), page_nvalid=i32(pn),
+                qt_qblock=i32(qq), qt_row0=i32(qr), qt_rows=i32(qn), qt_shape=i32(qs),
+                n_units=n_units, pl_ptr=pl_ptr, pl_pages=i32(pl),
+                useful=int(useful), physical=int(physical), n_ktiles=int(nkt))
+
+
+def build_plan_w(w) -> Plan:
+    return build_plan(w.B, w.Hq, w.Hkv, w.q_offsets, w.q_perm, w.k_offsets, w.k_perm, w.sel_nb, w.sel_nh,
+                      w.sel_row_ptr, w.sel_kblk, w.causal, w.q_pos0)
