@@ -1,0 +1,185 @@
+// C-ABI entry points of libbsattn (declared in include/bsattn.h).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <new>
+
+#include "bsattn.h"
+#include "kernel_params.hpp"
+#include "plan.hpp"
+
+namespace bsattn {
+hipError_t launch_fwd_shape(const FwdParams& p, int shape, int d, hipStream_t stream);
+}
+
+namespace {
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = int(e);
+  return BSATTN_E_HIP;
+}
+}  // namespace
+
+extern "C" {
+
+int bsattn_plan_create(const bsattn_problem* problem, const bsattn_layout* q_layout,
+                       const bsattn_layout* k_layout, const bsattn_selection* selection,
+                       int32_t page_size, bsattn_plan** out) {
+  if (out == nullptr) return BSATTN_E_ARG;
+  *out = nullptr;
+  if (problem == nullptr || q_layout == nullptr || k_layout == nullptr || selection == nullptr)
+    return BSATTN_E_ARG;
+  if (page_size != bsattn::kPage) return BSATTN_E_UNSUPPORTED;
+  bsattn_plan* p = new (std::nothrow) bsattn_plan();
+  if (p == nullptr) return BSATTN_E_OOM;
+  int st;
+  try {
+    st = bsattn::build_plan(*problem, *q_layout, *k_layout, *selection, p);
+  } catch (const std::bad_alloc&) {
+    st = BSATTN_E_OOM;
+  } catch (...) {
+    st = BSATTN_E_ARG;
+  }
+  if (st != BSATTN_OK) {
+    delete p;
+    return st;
+  }
+  *out = p;
+  return BSATTN_OK;
+}
+
+int bsattn_plan_device_bytes(const bsattn_plan* plan, size_t* bytes) {
+  if (plan == nullptr || bytes == nullptr) return BSATTN_E_ARG;
+  *bytes = plan->image.size();
+  return BSATTN_OK;
+}
+
+int bsattn_plan_upload(bsattn_plan* plan, void* dev, size_t bytes, void* stream) {
+  if (plan == nullptr || dev == nullptr) return BSATTN_E_ARG;
+  if (bytes < plan->image.size() || (reinterpret_cast<uintptr_t>(dev) & 255) != 0) return BSATTN_E_ARG;
+  hipError_t e = hipMemcpyAsync(dev, plan->image.data(), plan->image.size(), hipMemcpyHostToDevice,
+                                static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  plan->dev = dev;
+  return BSATTN_OK;
+}
+
+int bsattn_plan_stats(const bsattn_plan* plan, bsattn_stats* stats) {
+  if (plan == nullptr || stats == nullptr) return BSATTN_E_ARG;
+  *stats = plan->stats;
+  return BSATTN_OK;
+}
+
+int bsattn_plan_export(const bsattn_plan* plan, bsattn_plan_view* v) {
+  if (plan == nullptr || v == nullptr) return BSATTN_E_ARG;
+  v->n_pages = int64_t(plan->page_kblock.size());
+  v->page_kblock = plan->page_kblock.data();
+  v->page_slot0 = plan->page_slot0.data();
+  v->page_nvalid = plan->page_nvalid.data();
+  v->n_qtiles = int64_t(plan->qt_qblock.size());
+  v->qt_qblock = plan->qt_qblock.data();
+  v->qt_row0 = plan->qt_row0.data();
+  v->qt_rows = plan->qt_rows.data();
+  v->qt_shape = plan->qt_shape.data();
+  v->n_rows = int64_t(plan->pl_ptr.size()) - 1;
+  v->pl_ptr = plan->pl_ptr.data();
+  v->pl_pages = plan->pl_pages.data();
+  return BSATTN_OK;
+}
+
+}  // extern "C"
+
+namespace {
+// Validates the arguments and launches the kernels of the shapes in [sh0, sh1).
+int run_fwd(const bsattn_plan* plan, int sh0, int sh1, const void* q, const void* k, const void* v, void* o,
+            float* lse, float scale, void* stream) {
+  if (plan == nullptr) return BSATTN_E_ARG;
+  if (plan->dev == nullptr) return BSATTN_E_STATE;
+  const bsattn_problem& pr = plan->prob;
+  if (pr.Nq == 0) return BSATTN_OK;
+  if (q == nullptr || o == nullptr || lse == nullptr) return BSATTN_E_ARG;
+  if (pr.Nk > 0 && (k == nullptr || v == nullptr)) return BSATTN_E_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return BSATTN_E_ARG;
+  // every row must start on a 16-byte boundary: aligned bases and strides in multiples of 8
+  auto aligned = [](const void* ptr, const int64_t* st) {
+    return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0 && st[0] % 8 == 0 && st[1] % 8 == 0 && st[2] % 8 == 0;
+  };
+  if (!aligned(q, pr.q_stride) || !aligned(o, pr.o_stride)) return BSATTN_E_ARG;
+  if (pr.Nk > 0 && (!aligned(k, pr.k_stride) || !aligned(v, pr.v_stride))) return BSATTN_E_ARG;
+
+  const uint8_t* base = static_cast<const uint8_t*>(plan->dev);
+  bsattn::FwdParams fp{};
+  fp.q = q; fp.k = k; fp.v = v; fp.o = o; fp.lse = lse;
+  fp.q_sb = pr.q_stride[0]; fp.q_sn = pr.q_stride[1]; fp.q_sh = pr.q_stride[2];
+  fp.k_sb = pr.k_stride[0]; fp.k_sn = pr.k_stride[1]; fp.k_sh = pr.k_stride[2];
+  fp.v_sb = pr.v_stride[0]; fp.v_sn = pr.v_stride[1]; fp.v_sh = pr.v_stride[2];
+  fp.o_sb = pr.o_stride[0]; fp.o_sn = pr.o_stride[1]; fp.o_sh = pr.o_stride[2];
+  fp.pl_ptr = reinterpret_cast<const int32_t*>(base + plan->off_plptr);
+  fp.pl_ent = reinterpret_cast<const int32_t*>(base + plan->off_plent);
+  fp.qperm = plan->has_qperm ? reinterpret_cast<const int32_t*>(base + plan->off_qperm) : nullptr;
+  fp.kperm = plan->has_kperm ? reinterpret_cast<const int32_t*>(base + plan->off_kperm) : nullptr;
+  fp.q_pos0 = pr.q_pos0;
+  fp.B = pr.B; fp.Hq = pr.Hq; fp.Hkv = pr.Hkv; fp.Nq = pr.Nq; fp.Nk = pr.Nk;
+  fp.grp = pr.Hq / pr.Hkv;
+  fp.nqb = plan->nqb;
+  fp.sel_nh = plan->sel_nh;
+  fp.ub_mul = (plan->sel_nb == pr.B) ? 1 : 0;
+  fp.uh_div = (plan->sel_nh == pr.Hq) ? 1 : (plan->sel_nh == pr.Hkv ? fp.grp : pr.Hq);
+  fp.causal = pr.causal;
+  fp.scale = scale;
+  fp.scale_log2 = scale * 1.4426950408889634f;
+
+  const int64_t bh = int64_t(pr.B) * pr.Hq;
+  for (int sh = sh0; sh < sh1; ++sh) {
+    const int64_t nw = int64_t(plan->n_qt[sh]) * bh;
+    if (nw >= (int64_t(1) << 31)) return BSATTN_E_UNSUPPORTED;
+  }
+  for (int sh = sh0; sh < sh1; ++sh) {
+    bsattn::FwdParams f = fp;
+    f.qtiles = reinterpret_cast<const bsattn::QTileDev*>(base + plan->off_qt[sh]);
+    f.n_qtiles = plan->n_qt[sh];
+    f.n_work = int32_t(int64_t(plan->n_qt[sh]) * bh);
+    hipError_t e = bsattn::launch_fwd_shape(f, sh, pr.d, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return BSATTN_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int bsattn_fwd(const bsattn_plan* plan, const void* q, const void* k, const void* v, void* o, float* lse,
+               float scale, void* stream) {
+  return run_fwd(plan, 0, bsattn::kShapes, q, k, v, o, lse, scale, stream);
+}
+
+int bsattn_fwd_shape(const bsattn_plan* plan, int32_t shape, const void* q, const void* k, const void* v,
+                     void* o, float* lse, float scale, void* stream) {
+  if (shape < 0 || shape >= bsattn::kShapes) return BSATTN_E_ARG;
+  return run_fwd(plan, shape, shape + 1, q, k, v, o, lse, scale, stream);
+}
+
+int bsattn_plan_destroy(bsattn_plan* plan) {
+  delete plan;
+  return BSATTN_OK;
+}
+
+const char* bsattn_status_string(int status) {
+  switch (status) {
+    case BSATTN_OK: return "ok";
+    case BSATTN_E_ARG: return "invalid argument";
+    case BSATTN_E_LAYOUT: return "invalid token layout";
+    case BSATTN_E_SELECTION: return "invalid block selection";
+    case BSATTN_E_UNSUPPORTED: return "unsupported problem";
+    case BSATTN_E_OOM: return "host out of memory";
+    case BSATTN_E_HIP: return "HIP runtime error";
+    case BSATTN_E_STATE: return "plan not uploaded";
+    default: return "unknown status";
+  }
+}
+
+int bsattn_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

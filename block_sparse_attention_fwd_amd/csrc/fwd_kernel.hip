@@ -1,0 +1,383 @@
+// Exact block-sparse attention forward for gfx950 (MI355X).
+//
+// One workgroup (4 waves) owns one Q tile of one (batch, head) and walks its K tiles.
+// A K tile is 8 or 16 page-list entries; each entry is a 16-row K/V page of one block,
+// so a tile packs pages of several logical blocks (KPage abstract, zhuanzhiai page 1,
+// sentence 2).  Pages are gathered from HBM straight into LDS (global_load_lds, 16 bytes
+// per lane): nothing compacted is ever written back.  Q tiles come in two shapes
+// (sentence 3): 128 rows x 128 keys (4 row groups of 32 queries, one per wave) and 64 rows
+// x 256 keys (2 row groups x 2 key groups; the key groups keep separate softmax states
+// that are merged at the end).  Exact masking (sentence 4) clears empty page slots and,
+// for causal problems, keys after the query.
+//
+// Per wave and K tile the work is 32 queries x 128 keys:
+//   S^T = K Q^T    v_mfma_f32_32x32x16_bf16, A = K rows from LDS, B = Q^T in registers;
+//                  the accumulator gives each lane one query (lane % 32) and 64 keys.
+//   online softmax in fp32 (row max / sum per lane, one cross-half exchange),
+//                  exp2 with log2(e) folded into the scale.
+//   O^T += V^T P^T A = V^T read from LDS with ds_read_b64_tr_b16, B = P^T straight from
+//                  the score accumulators converted to bf16; the O^T accumulator again
+//                  gives each lane one query, so rescaling and the epilogue stay in-lane.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernel_params.hpp"
+
+namespace bsattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+#define LDS_AS __attribute__((address_space(3)))
+#define GLB_AS __attribute__((address_space(1)))
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
+// lgkmcnt[11:8] | vmcnt_hi[15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// XOR swizzle of the 16-byte chunk index inside an LDS row (d = 128: 16 chunks, d = 64:
+// 8 chunks).  Sixteen consecutive rows read at one logical chunk hit sixteen distinct
+// chunk slots (the K operand reads), and the 8 rows x 4 chunks of one transposed V read
+// land on every slot of a 256-byte bank line twice.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128) {
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+  } else {
+    const int m = (row >> 1) & 7;
+    return ((m & 1) << 2) | ((m >> 1) & 3);
+  }
+}
+
+// Workgroup barrier for LDS hand-off: publish this wave's LDS writes, then s_barrier.
+// Global->LDS loads are waited for explicitly (wait_vmcnt) before calling it.  The empty
+// asm statements keep the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), vmcnt/expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ float wave_xor32(float x) {
+  return __shfl_xor(x, 32, 64);
+}
+
+template <int D, int NRG, int NKG>
+struct Cfg {
+  static constexpr int kTileQ = 32 * NRG;
+  static constexpr int kTileK = 128 * NKG;
+  static constexpr int kPPT = kTileK / 16;           // pages per K tile
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kChunks = D / 8;              // 16-byte chunks per row
+  static constexpr int kRowsPerInst = 64 / kChunks;  // rows per 64-lane 16-byte load
+  static constexpr int kRowsPerWave = kTileK / 4;
+  static constexpr int kInst = kRowsPerWave / kRowsPerInst;  // loads per wave per tensor
+  static constexpr int kBufBytes = kTileK * kRowBytes;
+  static constexpr int kDS = D / 16;                 // k-steps of QK^T
+  static constexpr int kDB = D / 32;                 // 32-wide d blocks of O^T
+};
+
+template <int D, int NRG, int NKG>
+__global__ void __launch_bounds__(256) fwd_kernel(FwdParams p) {
+  using C = Cfg<D, NRG, NKG>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_k[C::kBufBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_v[C::kBufBytes];
+  __shared__ int ktok_lds[C::kTileK];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = wave % NRG;
+  const int kg = wave / NRG;
+  const int hh = lane >> 5;
+
+  // ---- work item (XCD-aware: consecutive items share an XCD's L2) ----
+  int work;
+  {
+    const int n = p.n_work, blk = blockIdx.x;
+    const int x = blk & 7, i = blk >> 3, q = n >> 3, r = n & 7;
+    work = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
+  }
+  const int bh = work / p.n_qtiles;
+  const int t = work - bh * p.n_qtiles;
+  const int b = bh / p.Hq;
+  const int h = bh - b * p.Hq;
+  const int g = h / p.grp;
+  const QTileDev qt = p.qtiles[t];
+  const int unit = (b * p.ub_mul) * p.sel_nh + h / p.uh_div;
+  const int row = unit * p.nqb + qt.qblock;
+  const int e0 = p.pl_ptr[row];
+  const int e1 = p.pl_ptr[row + 1];
+  const int nkt = (e1 - e0 + C::kPPT - 1) / C::kPPT;
+
+  // ---- Q^T operand: lane holds query (lane % 32) of its row group, 8 d per k-step ----
+  const int qrow = rg * 32 + (lane & 31);
+  const bool qvalid = qrow < qt.rows;
+  const int qslot = qt.row0 + (qvalid ? qrow : 0);
+  const int qtok = p.qperm ? p.qperm[qslot] : qslot;
+  bf16x8 qreg[C::kDS];
+  {
+    const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.q_sb + (int64_t)qtok * p.q_sn +
+                       (int64_t)h * p.q_sh + hh * 8;
+#pragma unroll
+    for (int s = 0; s < C::kDS; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
+  }
+  // causal threshold for this lane's query: a key is kept iff its token <= thr
+  int thr = 0x7ffffffe;
+  if (p.causal) {
+    const int64_t qp = p.q_pos0 + (int64_t)qtok;
+    thr = qp < -1 ? -1 : (qp > 0x7ffffffe ? 0x7ffffffe : (int)qp);
+  }
+
+  // ---- loader: which rows this lane moves, and where ----
+  const int ld_lr = lane / C::kChunks;    // row inside one load
+  const int ld_pc = lane % C::kChunks;    // physical chunk slot this lane fills
+  const __bf16* kbase = reinterpret_cast<const __bf16*>(p.k) + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh;
+  const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v) + (int64_t)b * p.v_sb + (int64_t)g * p.v_sh;
+  int ldtok[C::kInst];
+
+  // Tokens of the rows this lane loads for K tile kt (also published to ktok_lds, with
+  // empty slots marked), and whether this wave's 128-key slice of the tile needs masking.
+  // The page of every load instruction is wave-uniform: a 16-row page spans whole loads.
+  constexpr int kWavePages = C::kRowsPerWave / 16;
+  auto fetch_tokens = [&](int kt) -> bool {
+    const int etile = e0 + kt * C::kPPT;
+    int ents[kWavePages];
+#pragma unroll
+    for (int pp = 0; pp < kWavePages; ++pp) {
+      const int e = etile + wave * kWavePages + pp;
+      const int ent = p.pl_ent[e < e1 ? e : e1 - 1];
+      ents[pp] = e < e1 ? ent : 0;
+    }
+#pragma unroll
+    for (int n = 0; n < C::kInst; ++n) {
+      const int r = wave * C::kRowsPerWave + n * C::kRowsPerInst + ld_lr;
+      const int ent = ents[(n * C::kRowsPerInst) >> 4];
+      const int nv = ent & 31;
+      const int rip = r & 15;
+      const int slot = (ent >> 5) + (rip < nv ? rip : 0);
+      ldtok[n] = p.kperm ? p.kperm[slot] : slot;
+    }
+#pragma unroll
+    for (int n = 0; n < C::kInst; ++n) {
+      const int r = wave * C::kRowsPerWave + n * C::kRowsPerInst + ld_lr;
+      const int nv = ents[(n * C::kRowsPerInst) >> 4] & 31;
+      if (ld_pc == 0) ktok_lds[r] = (r & 15) < nv ? ldtok[n] : 0x7fffffff;
+    }
+    bool need = false;
+    int maxkey = -1;
+#pragma unroll
+    for (int pp = 0; pp < 8; ++pp) {
+      const int e = etile + kg * 8 + pp;
+      const int ent = p.pl_ent[e < e1 ? e : e1 - 1];
+      const int nv = e < e1 ? (ent & 31) : 0;
+      need |= nv < 16;
+      const int last = (ent >> 5) + nv - 1;
+      maxkey = (e < e1 && last > maxkey) ? last : maxkey;
+    }
+    if (p.causal) {
+      if (p.kperm || p.qperm)
+        need = true;
+      else
+        need |= (int64_t)maxkey > p.q_pos0 + qt.row0 + rg * 32;
+    }
+    return need;
+  };
+  auto issue = [&](const __bf16* base, int64_t sn, uint8_t* buf) {
+#pragma unroll
+    for (int n = 0; n < C::kInst; ++n) {
+      const int r = wave * C::kRowsPerWave + n * C::kRowsPerInst + ld_lr;
+      const int c = ld_pc ^ swz<D>(r);
+      const __bf16* src = base + (int64_t)ldtok[n] * sn + c * 8;
+      uint8_t* dst = buf + (wave * C::kRowsPerWave + n * C::kRowsPerInst) * C::kRowBytes;
+      __builtin_amdgcn_global_load_lds((const GLB_AS void*)src, (LDS_AS void*)dst, 16, 0, 0);
+    }
+  };
+
+  // ---- running softmax state and O^T accumulators ----
+  float m_run = kNegInf;
+  float l_run = 0.f;
+  f32x16 oacc[C::kDB];
+#pragma unroll
+  for (int db = 0; db < C::kDB; ++db) oacc[db] = f32x16{};
+
+  const float sl2 = p.scale_log2;
+  const int kbase_row = kg * 128;
+
+  bool nm_next = false;
+  if (nkt > 0) {
+    nm_next = fetch_tokens(0);
+    issue(kbase, p.k_sn, smem_k);
+    issue(vbase, p.v_sn, smem_v);
+  }
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    const bool need_mask = nm_next;
+
+    wait_vmcnt<C::kInst>();  // K tile landed (V may still be in flight)
+    lds_barrier();
+
+    // ---- S^T = K Q^T ----
+    f32x16 sacc[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) sacc[kb] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < C::kDS; ++s) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int r = kbase_row + 32 * kb + (lane & 31);
+        const int c = (2 * s + hh) ^ swz<D>(r);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(smem_k + r * C::kRowBytes + c * 16);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], sacc[kb], 0, 0, 0);
+      }
+    }
+
+    // ---- exact mask: empty page slots, causally hidden keys ----
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const i32x4 kt4 = *reinterpret_cast<const i32x4*>(&ktok_lds[kbase_row + 32 * kb + 8 * i + 4 * hh]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (kt4[j] > thr) sacc[kb][4 * i + j] = kNegInf;
+        }
+      }
+    }
+
+    // ---- online softmax ----
+    float mt = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[kb][e]);
+    mt = fmaxf(mt, wave_xor32(mt));
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * sl2);
+    const float nb = -m_use * sl2;
+    float lsum = 0.f;
+    bf16x8 pb[8];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][e], sl2, nb));
+        lsum += pe;
+        pb[2 * kb + (e >> 3)][e & 7] = (__bf16)pe;
+      }
+    }
+    l_run = l_run * alpha + lsum;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < C::kDB; ++db) oacc[db] *= alpha;
+
+    wait_vmcnt<0>();  // V tile landed
+    lds_barrier();    // every wave is done with the K buffer and the token list
+    if (kt + 1 < nkt) {
+      nm_next = fetch_tokens(kt + 1);
+      issue(kbase, p.k_sn, smem_k);
+    }
+
+    // ---- O^T += V^T P^T ----
+    {
+      const int G = lane >> 4, w16 = lane & 15, rr = w16 >> 2, qq = w16 & 3, dsub = G & 1;
+#pragma unroll
+      for (int c16 = 0; c16 < 8; ++c16) {
+        const int key_a = kbase_row + 16 * c16 + 4 * hh + rr;
+        const int key_b = key_a + 8;
+#pragma unroll
+        for (int db = 0; db < C::kDB; ++db) {
+          const int lc = 4 * db + 2 * dsub + (qq >> 1);
+          const int off_in = (qq & 1) * 8;
+          const LDS_AS bf16x4* pa =
+              (const LDS_AS bf16x4*)(smem_v + key_a * C::kRowBytes + ((lc ^ swz<D>(key_a)) * 16) + off_in);
+          const LDS_AS bf16x4* pbp =
+              (const LDS_AS bf16x4*)(smem_v + key_b * C::kRowBytes + ((lc ^ swz<D>(key_b)) * 16) + off_in);
+          const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)pa);
+          const bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)pbp);
+          const bf16x8 av = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[c16], oacc[db], 0, 0, 0);
+        }
+      }
+    }
+
+    lds_barrier();  // every wave is done with the V buffer
+    if (kt + 1 < nkt) issue(vbase, p.v_sn, smem_v);
+  }
+
+  // ---- finish: combine lane halves, merge key groups, write O and LSE ----
+  float l_tot = l_run + wave_xor32(l_run);
+  float m_fin = m_run;
+  if constexpr (NKG == 2) {
+    // key group 1 hands (m, l, O^T) to key group 0 through LDS (the K buffer is free)
+    __syncthreads();
+    float* mb = reinterpret_cast<float*>(smem_k) + rg * (C::kDB * 16 + 2) * 64;
+    if (kg == 1) {
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mb[(db * 16 + e) * 64 + lane] = oacc[db][e];
+      mb[(C::kDB * 16) * 64 + lane] = m_run;
+      mb[(C::kDB * 16 + 1) * 64 + lane] = l_tot;
+    }
+    __syncthreads();
+    if (kg == 1) return;
+    const float m1 = mb[(C::kDB * 16) * 64 + lane];
+    const float l1 = mb[(C::kDB * 16 + 1) * 64 + lane];
+    const float mm = fmaxf(m_run, m1);
+    const float mu = (mm == kNegInf) ? 0.f : mm;
+    const float a0 = __builtin_amdgcn_exp2f((m_run - mu) * sl2);
+    const float a1 = __builtin_amdgcn_exp2f((m1 - mu) * sl2);
+#pragma unroll
+    for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[db][e] = oacc[db][e] * a0 + mb[(db * 16 + e) * 64 + lane] * a1;
+    l_tot = l_tot * a0 + l1 * a1;
+    m_fin = mm;
+  }
+
+  if (!qvalid) return;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  __bf16* op = reinterpret_cast<__bf16*>(p.o) + (int64_t)b * p.o_sb + (int64_t)qtok * p.o_sn + (int64_t)h * p.o_sh;
+#pragma unroll
+  for (int db = 0; db < C::kDB; ++db) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bf16x4 v4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v4[j] = (__bf16)(oacc[db][4 * i + j] * inv);
+      *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * i + 4 * hh) = v4;
+    }
+  }
+  if (hh == 0) {
+    const float lse = l_tot > 0.f ? m_fin * p.scale + __logf(l_tot) : kNegInf;
+    p.lse[((int64_t)b * p.Hq + h) * p.Nq + qtok] = lse;
+  }
+}
+
+template <int D, int NRG, int NKG>
+static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
+  if (p.n_work <= 0) return hipSuccess;
+  hipLaunchKernelGGL((fwd_kernel<D, NRG, NKG>), dim3(p.n_work), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_shape(const FwdParams& p, int shape, int d, hipStream_t stream) {
+  if (d == 128) return shape == 0 ? launch_one<128, 4, 1>(p, stream) : launch_one<128, 2, 2>(p, stream);
+  return shape == 0 ? launch_one<64, 4, 1>(p, stream) : launch_one<64, 2, 2>(p, stream);
+}
+
+}  // namespace bsattn

@@ -1,0 +1,40 @@
+// Arguments of the forward kernels (passed by value) and the device Q-tile record.
+#pragma once
+
+#include <cstdint>
+
+namespace bsattn {
+
+// One Q tile as the kernel reads it.
+struct QTileDev {
+  int32_t row0;    // first slot in the Q layout
+  int32_t rows;    // valid rows
+  int32_t qblock;  // Q block id
+  int32_t pad;
+};
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t q_sb, q_sn, q_sh;
+  int64_t k_sb, k_sn, k_sh;
+  int64_t v_sb, v_sn, v_sh;
+  int64_t o_sb, o_sn, o_sh;
+  const QTileDev* qtiles;     // Q tiles of one shape
+  const int32_t* pl_ptr;      // [n_units * nqb + 1]
+  const int32_t* pl_ent;      // packed (first slot << 5) | valid rows
+  const int32_t* qperm;       // slot -> token, or null
+  const int32_t* kperm;
+  int64_t q_pos0;
+  int32_t n_qtiles;           // tiles of this shape
+  int32_t n_work;             // n_qtiles * B * Hq
+  int32_t B, Hq, Hkv, Nq, Nk, grp;
+  int32_t nqb, sel_nh, ub_mul, uh_div;
+  int32_t causal;
+  float scale, scale_log2;
+};
+
+}  // namespace bsattn

@@ -1,0 +1,241 @@
+// Host planner.  Rules (a reading of KPage abstract sentences 2-4 and 7, zhuanzhiai page 1):
+//   selection  a (unit, Q block) row selects a set of K blocks (sorted, duplicates dropped);
+//   pages      a K block of n slots has ceil(n/16) pages, page p covering its slots
+//              [16p, min(16p+16, n)); empty blocks have none;
+//   routing    a Q block of n rows gives floor(n/128) 128-row tiles, then one 64-row tile
+//              when 0 < n mod 128 <= 64, or one more 128-row tile when n mod 128 > 64;
+//   K tiles    a Q tile's page list (selected blocks ascending, pages ascending) is cut
+//              into ceil(pages / pages-per-tile) tiles of 8 (128x128) or 16 (64x256) pages;
+//   counts     useful = graph pairs; physical = tile rows x tile cols x K tiles, summed
+//              over every (batch, head) and Q tile.
+#include "plan.hpp"
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+
+namespace bsattn {
+namespace {
+
+int check_layout(const bsattn_layout& l, int32_t n_tokens, std::vector<int32_t>* token_of_slot) {
+  if (l.n_blocks < 0 || l.offsets == nullptr) return BSATTN_E_ARG;
+  if (l.offsets[0] != 0 || l.offsets[l.n_blocks] != n_tokens) return BSATTN_E_LAYOUT;
+  for (int32_t b = 0; b < l.n_blocks; ++b)
+    if (l.offsets[b + 1] < l.offsets[b]) return BSATTN_E_LAYOUT;
+  token_of_slot->resize(size_t(n_tokens));
+  if (l.perm == nullptr) {
+    for (int32_t s = 0; s < n_tokens; ++s) (*token_of_slot)[s] = s;
+    return BSATTN_OK;
+  }
+  std::vector<uint8_t> seen(size_t(n_tokens), 0);
+  for (int32_t s = 0; s < n_tokens; ++s) {
+    int32_t t = l.perm[s];
+    if (t < 0 || t >= n_tokens || seen[t]) return BSATTN_E_LAYOUT;
+    seen[t] = 1;
+    (*token_of_slot)[s] = t;
+  }
+  return BSATTN_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+int build_plan(const bsattn_problem& prob, const bsattn_layout& ql, const bsattn_layout& kl,
+               const bsattn_selection& sel, bsattn_plan* p) {
+  const int32_t B = prob.B, Hq = prob.Hq, Hkv = prob.Hkv, Nq = prob.Nq, Nk = prob.Nk;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 0 || Nk < 0 || Hq % Hkv != 0) return BSATTN_E_ARG;
+  if (prob.causal != 0 && prob.causal != 1) return BSATTN_E_ARG;
+  if (prob.d != 64 && prob.d != 128) return BSATTN_E_UNSUPPORTED;
+  if (prob.dtype != BSATTN_DTYPE_BF16) return BSATTN_E_UNSUPPORTED;
+  if (int64_t(Nk) >= kMaxSlots || int64_t(Nq) >= kMaxSlots) return BSATTN_E_UNSUPPORTED;
+  if (int64_t(B) * Hq > (int64_t(1) << 24)) return BSATTN_E_UNSUPPORTED;
+
+  std::vector<int32_t> qtok, ktok;
+  int st = check_layout(ql, Nq, &qtok);
+  if (st != BSATTN_OK) return st;
+  st = check_layout(kl, Nk, &ktok);
+  if (st != BSATTN_OK) return st;
+
+  const int32_t nqb = ql.n_blocks, nkb = kl.n_blocks;
+  if (sel.n_b != 1 && sel.n_b != B) return BSATTN_E_SELECTION;
+  if (sel.n_h != 1 && sel.n_h != Hkv && sel.n_h != Hq) return BSATTN_E_SELECTION;
+  if (sel.row_ptr == nullptr) return BSATTN_E_ARG;
+  const int64_t n_units = int64_t(sel.n_b) * sel.n_h;
+  const int64_t n_rows = n_units * nqb;
+  if (sel.row_ptr[0] != 0) return BSATTN_E_SELECTION;
+  for (int64_t r = 0; r < n_rows; ++r)
+    if (sel.row_ptr[r + 1] < sel.row_ptr[r]) return BSATTN_E_SELECTION;
+  if (sel.row_ptr[n_rows] > 0 && sel.kblk == nullptr) return BSATTN_E_ARG;
+  for (int64_t e = 0; e < sel.row_ptr[n_rows]; ++e)
+    if (sel.kblk[e] < 0 || sel.kblk[e] >= nkb) return BSATTN_E_SELECTION;
+
+  p->prob = prob;
+  p->nqb = nqb;
+  p->nkb = nkb;
+  p->sel_nb = sel.n_b;
+  p->sel_nh = sel.n_h;
+  p->n_units = int32_t(n_units);
+
+  // pages
+  std::vector<int32_t> first_page(size_t(nkb) + 1, 0);
+  for (int32_t kb = 0; kb < nkb; ++kb) {
+    const int32_t s0 = kl.offsets[kb], n = kl.offsets[kb + 1] - s0;
+    for (int32_t pg = 0; pg * kPage < n; ++pg) {
+      p->page_kblock.push_back(kb);
+      p->page_slot0.push_back(s0 + pg * kPage);
+      p->page_nvalid.push_back(std::min(kPage, n - pg * kPage));
+    }
+    first_page[kb + 1] = int32_t(p->page_kblock.size());
+  }
+
+  // Q routing
+  for (int32_t qb = 0; qb < nqb; ++qb) {
+    const int32_t s0 = ql.offsets[qb], n = ql.offsets[qb + 1] - s0;
+    const int32_t full = n / 128, r = n % 128;
+    for (int32_t t = 0; t < full; ++t) {
+      p->qt_qblock.push_back(qb); p->qt_row0.push_back(s0 + 128 * t);
+      p->qt_rows.push_back(128); p->qt_shape.push_back(BSATTN_SHAPE_128x128);
+    }
+    if (r > 0) {
+      p->qt_qblock.push_back(qb); p->qt_row0.push_back(s0 + 128 * full);
+      p->qt_rows.push_back(r);
+      p->qt_shape.push_back(r <= 64 ? BSATTN_SHAPE_64x256 : BSATTN_SHAPE_128x128);
+    }
+  }
+
+  // page lists per (unit, Q block), and per-row selected-key totals for the counts
+  p->pl_ptr.assign(size_t(n_rows) + 1, 0);
+  std::vector<int32_t> row_sel;
+  std::vector<std::vector<int32_t>> row_blocks(static_cast<size_t>(n_rows));
+  for (int64_t r = 0; r < n_rows; ++r) {
+    row_sel.assign(sel.kblk + sel.row_ptr[r], sel.kblk + sel.row_ptr[r + 1]);
+    std::sort(row_sel.begin(), row_sel.end());
+    row_sel.erase(std::unique(row_sel.begin(), row_sel.end()), row_sel.end());
+    for (int32_t kb : row_sel)
+      for (int32_t pg = first_page[kb]; pg < first_page[kb + 1]; ++pg) p->pl_pages.push_back(pg);
+    p->pl_ptr[r + 1] = int64_t(p->pl_pages.size());
+    row_blocks[r] = row_sel;
+  }
+  if (p->pl_pages.size() >= (size_t(1) << 31)) return BSATTN_E_UNSUPPORTED;
+
+  // useful pairs per (unit, shape): a non-causal tile holds rows * (selected keys) pairs;
+  // a causal tile counts, per query, the selected keys at positions <= q_pos0 + token.
+  std::vector<std::vector<int32_t>> ksorted;
+  if (prob.causal) {
+    ksorted.resize(size_t(nkb));
+    for (int32_t kb = 0; kb < nkb; ++kb) {
+      ksorted[kb].assign(ktok.begin() + kl.offsets[kb], ktok.begin() + kl.offsets[kb + 1]);
+      std::sort(ksorted[kb].begin(), ksorted[kb].end());
+    }
+  }
+  std::vector<int64_t> nk_row(size_t(n_rows), 0);
+  for (int64_t r = 0; r < n_rows; ++r)
+    for (int32_t kb : row_blocks[size_t(r)]) nk_row[size_t(r)] += kl.offsets[kb + 1] - kl.offsets[kb];
+  const size_t nt = p->qt_qblock.size();
+  std::vector<int64_t> unit_use(size_t(n_units) * kShapes, 0), unit_phys(size_t(n_units) * kShapes, 0);
+  std::vector<int64_t> unit_kt(size_t(n_units), 0);
+  std::vector<int64_t> qpos;
+  for (int64_t u = 0; u < n_units; ++u) {
+    for (size_t t = 0; t < nt; ++t) {
+      const int sh = p->qt_shape[t];
+      const int64_t row = u * nqb + p->qt_qblock[t];
+      const int64_t npg = p->pl_ptr[size_t(row) + 1] - p->pl_ptr[size_t(row)];
+      const int64_t k = (npg + kPagesPerKTile[sh] - 1) / kPagesPerKTile[sh];
+      unit_kt[size_t(u)] += k;
+      unit_phys[size_t(u) * kShapes + sh] += int64_t(kTileRows[sh]) * kTileCols[sh] * k;
+      const auto& blocks = row_blocks[size_t(row)];
+      if (blocks.empty()) continue;
+      if (!prob.causal) {
+        unit_use[size_t(u) * kShapes + sh] += int64_t(p->qt_rows[t]) * nk_row[size_t(row)];
+        continue;
+      }
+      qpos.clear();
+      for (int32_t s = p->qt_row0[t]; s < p->qt_row0[t] + p->qt_rows[t]; ++s) qpos.push_back(prob.q_pos0 + qtok[s]);
+      std::sort(qpos.begin(), qpos.end());
+      int64_t tot = 0;
+      for (int32_t kb : blocks) {
+        const auto& ks = ksorted[kb];
+        if (ks.empty()) continue;
+        if (int64_t(ks.back()) <= qpos.front()) { tot += int64_t(ks.size()) * int64_t(qpos.size()); continue; }
+        if (int64_t(ks.front()) > qpos.back()) continue;
+        for (int64_t qp : qpos)
+          tot += int64_t(std::upper_bound(ks.begin(), ks.end(), qp,
+                                          [](int64_t a, int32_t b) { return a < int64_t(b); }) - ks.begin());
+      }
+      unit_use[size_t(u) * kShapes + sh] += tot;
+    }
+  }
+
+  // sum over every (b, h) through its unit
+  const int32_t grp = Hq / Hkv;
+  int64_t useful = 0, physical = 0, nkt = 0;
+  int64_t use_sh[kShapes] = {0, 0}, phys_sh[kShapes] = {0, 0};
+  for (int32_t b = 0; b < B; ++b) {
+    for (int32_t h = 0; h < Hq; ++h) {
+      const int32_t ub = (sel.n_b == B) ? b : 0;
+      const int32_t uh = (sel.n_h == Hq) ? h : (sel.n_h == Hkv ? h / grp : 0);
+      const size_t u = size_t(int64_t(ub) * sel.n_h + uh);
+      for (int sh = 0; sh < kShapes; ++sh) {
+        use_sh[sh] += unit_use[u * kShapes + sh];
+        phys_sh[sh] += unit_phys[u * kShapes + sh];
+      }
+      nkt += unit_kt[u];
+    }
+  }
+  for (int sh = 0; sh < kShapes; ++sh) {
+    useful += use_sh[sh];
+    physical += phys_sh[sh];
+    p->stats.useful_by_shape[sh] = use_sh[sh];
+    p->stats.physical_by_shape[sh] = phys_sh[sh];
+  }
+  p->stats.useful = useful;
+  p->stats.physical = physical;
+  p->stats.n_pages = int64_t(p->page_kblock.size());
+  p->stats.n_qtiles128 = std::count(p->qt_shape.begin(), p->qt_shape.end(), int32_t(BSATTN_SHAPE_128x128));
+  p->stats.n_qtiles64 = std::count(p->qt_shape.begin(), p->qt_shape.end(), int32_t(BSATTN_SHAPE_64x256));
+  p->stats.n_ktiles = nkt;
+  p->stats.page_list_len = int64_t(p->pl_pages.size());
+  p->stats.n_units = n_units;
+
+  // device image: Q tiles per shape, page-list pointers, packed page entries, perms
+  size_t off = 0;
+  for (int sh = 0; sh < kShapes; ++sh) {
+    p->off_qt[sh] = off;
+    p->n_qt[sh] = int32_t(std::count(p->qt_shape.begin(), p->qt_shape.end(), sh));
+    off = align256(off + sizeof(QTileDev) * size_t(p->n_qt[sh]));
+  }
+  p->off_plptr = off;
+  off = align256(off + sizeof(int32_t) * (size_t(n_rows) + 1));
+  p->off_plent = off;
+  off = align256(off + sizeof(int32_t) * p->pl_pages.size());
+  p->has_qperm = ql.perm != nullptr;
+  p->has_kperm = kl.perm != nullptr;
+  p->off_qperm = off;
+  if (p->has_qperm) off = align256(off + sizeof(int32_t) * size_t(Nq));
+  p->off_kperm = off;
+  if (p->has_kperm) off = align256(off + sizeof(int32_t) * size_t(Nk));
+  p->image.assign(std::max<size_t>(off, 256), 0);
+
+  uint8_t* img = p->image.data();
+  for (int sh = 0; sh < kShapes; ++sh) {
+    QTileDev* q = reinterpret_cast<QTileDev*>(img + p->off_qt[sh]);
+    int32_t i = 0;
+    for (size_t t = 0; t < p->qt_shape.size(); ++t) {
+      if (p->qt_shape[t] != sh) continue;
+      q[i++] = QTileDev{p->qt_row0[t], p->qt_rows[t], p->qt_qblock[t], 0};
+    }
+  }
+  int32_t* plp = reinterpret_cast<int32_t*>(img + p->off_plptr);
+  for (size_t r = 0; r <= size_t(n_rows); ++r) plp[r] = int32_t(p->pl_ptr[r]);
+  int32_t* ent = reinterpret_cast<int32_t*>(img + p->off_plent);
+  for (size_t e = 0; e < p->pl_pages.size(); ++e) {
+    const int32_t pg = p->pl_pages[e];
+    ent[e] = (p->page_slot0[pg] << kEntryShift) | p->page_nvalid[pg];
+  }
+  if (p->has_qperm) std::memcpy(img + p->off_qperm, ql.perm, sizeof(int32_t) * size_t(Nq));
+  if (p->has_kperm) std::memcpy(img + p->off_kperm, kl.perm, sizeof(int32_t) * size_t(Nk));
+  return BSATTN_OK;
+}
+
+}  // namespace bsattn

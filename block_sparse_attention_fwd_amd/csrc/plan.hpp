@@ -1,0 +1,52 @@
+// Host-side plan: K/V pages, Q-tile routing, page lists and pair counts.
+//
+// KPage abstract (zhuanzhiai page 1): sentence 2 -- 16-row K/V pages of valid tokens,
+// packed across logical-block boundaries into large tiles while loading; sentence 3 --
+// Q blocks routed between 64x256 and 128x128 tiles; sentence 4 -- pages are owned by
+// one K/V block and masking is exact; sentence 7 -- physical vs useful pair capacity.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "bsattn.h"
+#include "kernel_params.hpp"
+
+namespace bsattn {
+
+constexpr int kPage = 16;
+constexpr int kShapes = 2;
+constexpr int kTileRows[kShapes] = {128, 64};
+constexpr int kTileCols[kShapes] = {128, 256};
+constexpr int kPagesPerKTile[kShapes] = {8, 16};
+// page-list entries are packed as (first slot << 5) | valid rows
+constexpr int kEntryShift = 5;
+constexpr int64_t kMaxSlots = int64_t(1) << (31 - kEntryShift);
+
+}  // namespace bsattn
+
+struct bsattn_plan {
+  bsattn_problem prob{};
+  int32_t nqb = 0, nkb = 0, sel_nb = 1, sel_nh = 1, n_units = 1;
+  // canonical arrays (exported)
+  std::vector<int32_t> page_kblock, page_slot0, page_nvalid;
+  std::vector<int32_t> qt_qblock, qt_row0, qt_rows, qt_shape;
+  std::vector<int64_t> pl_ptr;
+  std::vector<int32_t> pl_pages;
+  bsattn_stats stats{};
+  // device image, staged on the host; offsets are byte offsets into it
+  std::vector<uint8_t> image;
+  size_t off_qt[bsattn::kShapes] = {0, 0};
+  int32_t n_qt[bsattn::kShapes] = {0, 0};
+  size_t off_plptr = 0, off_plent = 0, off_qperm = 0, off_kperm = 0;
+  bool has_qperm = false, has_kperm = false;
+  // bound device buffer (caller-owned)
+  void* dev = nullptr;
+};
+
+namespace bsattn {
+// Builds *p from validated arguments; returns a bsattn_status.
+int build_plan(const bsattn_problem& prob, const bsattn_layout& ql, const bsattn_layout& kl,
+               const bsattn_selection& sel, bsattn_plan* p);
+}  // namespace bsattn

@@ -1,0 +1,180 @@
+/*
+ * bsattn -- exact block-sparse softmax attention forward for AMD MI355X (gfx950).
+ *
+ * The operation (KPage abstract, zhuanzhiai page 1, sentences 2-4; FlashAttention
+ * entries of the scifaro related-paper lists for the softmax / log-sum-exp convention):
+ *
+ *   For batch b, query head h (KV head g = h / (Hq / Hkv)), query token i and key token j,
+ *   the pair (i, j) is in the sparse graph iff the K block holding j is in the selected
+ *   set of the Q block holding i (for the selection unit of (b, h)) and, when the problem
+ *   is causal, j <= q_pos0 + i.  Then
+ *       O[b, i, h, :] = sum_j softmax_j(scale * <Q[b,i,h,:], K[b,j,g,:]>) V[b, j, g, :]
+ *       LSE[b, h, i]  = ln sum_j exp(scale * <Q[b,i,h,:], K[b,j,g,:]>)
+ *   over the graph's keys only.  A query with no key gets O = 0 and LSE = -inf.
+ *
+ * How it is computed (same abstract, sentences 2-3): every K block is cut into 16-row
+ * pages of valid tokens, each owned by that block; the pages selected by a Q block are
+ * packed, across block boundaries, into K tiles of 8 pages (128 keys) or 16 pages
+ * (256 keys) as they are loaded into LDS -- no compacted copy is written to HBM.  Q
+ * blocks are routed between 128-row tiles (128x128) and 64-row tiles (64x256) so that a
+ * small Q block does not pad to 128 rows.  Masking is exact: empty page slots, padded
+ * query rows and causally hidden keys never contribute.
+ *
+ * Conventions
+ *   - Every call returns an int status: BSATTN_OK (0) or one of the BSATTN_E_* codes.
+ *     No C++ exception crosses this interface.  bsattn_status_string() names a code.
+ *   - Host arrays passed in (layouts, selections) are read during the call only.
+ *   - All device memory is owned by the caller: the library never allocates device
+ *     memory.  Streams are hipStream_t values passed as void* (NULL = default stream).
+ *   - A plan is immutable once uploaded and may be used from several host threads;
+ *     bsattn_fwd calls that share a plan may run concurrently on different streams.
+ */
+#ifndef BSATTN_H_
+#define BSATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum bsattn_status {
+  BSATTN_OK = 0,
+  BSATTN_E_ARG = 1,          /* null pointer, bad size or count, plan/argument mismatch */
+  BSATTN_E_LAYOUT = 2,       /* offsets not rising from 0 to N, or perm not a permutation */
+  BSATTN_E_SELECTION = 3,    /* selection CSR malformed or a block id out of range */
+  BSATTN_E_UNSUPPORTED = 4,  /* head_dim not 64/128, dtype not bf16, page size not 16, sizes past limits */
+  BSATTN_E_OOM = 5,          /* host allocation failed */
+  BSATTN_E_HIP = 6,          /* a HIP runtime call failed (see bsattn_last_hip_error) */
+  BSATTN_E_STATE = 7         /* plan not uploaded to device memory */
+};
+
+enum { BSATTN_DTYPE_BF16 = 1 };
+
+/* Tile shapes (KPage abstract, sentence 3): rows of the Q tile x columns of the K tile. */
+enum { BSATTN_SHAPE_128x128 = 0, BSATTN_SHAPE_64x256 = 1 };
+
+/* Problem shape.  Tensors are Q [B, Nq, Hq, d], K and V [B, Nk, Hkv, d], O like Q, all
+ * bf16 with d contiguous; the *_stride arrays give the element strides of the batch,
+ * token and head dimensions.  LSE is float32 [B, Hq, Nq], contiguous.  For a causal
+ * problem, query token i sits at absolute position q_pos0 + i and key token j at j. */
+typedef struct bsattn_problem {
+  int32_t B, Hq, Hkv, Nq, Nk, d;
+  int32_t dtype;     /* BSATTN_DTYPE_BF16 */
+  int32_t causal;    /* 0 or 1 */
+  int64_t q_pos0;
+  int64_t q_stride[3];
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];
+} bsattn_problem;
+
+/* Token layout of one side, shared by every batch and head.  Block k holds the slots
+ * [offsets[k], offsets[k+1]); slot s holds token perm[s] (token s when perm is NULL).
+ * offsets must rise from 0 to N; perm, when given, must be a permutation of [0, N).
+ * Empty blocks are allowed. */
+typedef struct bsattn_layout {
+  int32_t n_blocks;
+  const int32_t* offsets; /* [n_blocks + 1] */
+  const int32_t* perm;    /* [N] or NULL */
+} bsattn_layout;
+
+/* Block selection as CSR over rows (unit, Q block), row = unit * n_qblocks + qblock,
+ * unit = ub * n_h + uh.  n_b is 1 (shared by all batches, ub = 0) or B (ub = b).  n_h is
+ * Hq (uh = h), Hkv (uh = h / (Hq/Hkv): one selection per KV group, shared by the group's
+ * query heads -- CISA abstract, fugumt page 4, sentence 4) or 1 (uh = 0).  When Hq equals
+ * Hkv the two readings coincide.  A row lists selected K block ids in any order;
+ * duplicates count once. */
+typedef struct bsattn_selection {
+  int32_t n_b, n_h;
+  const int32_t* row_ptr; /* [n_b * n_h * n_qblocks + 1], rising from 0 */
+  const int32_t* kblk;    /* [row_ptr[last]], each in [0, n_kblocks) */
+} bsattn_selection;
+
+/* Plan statistics (KPage abstract, sentence 7: useful vs physical query-key pairs).
+ * useful   = pairs of the sparse graph over all (batch, head), causal exclusions removed;
+ * physical = sum over (batch, head) and Q tiles of tile_rows * tile_cols * K tiles,
+ *            padded rows and empty page slots included. */
+typedef struct bsattn_stats {
+  int64_t useful;
+  int64_t physical;
+  int64_t n_pages;        /* K pages of the layout */
+  int64_t n_qtiles128;    /* Q tiles of the layout routed to 128x128 */
+  int64_t n_qtiles64;     /* Q tiles of the layout routed to 64x256 */
+  int64_t n_ktiles;       /* K tiles over all (batch, head, Q tile) work items */
+  int64_t page_list_len;  /* entries of all (unit, Q block) page lists */
+  int64_t n_units;        /* selection units */
+  int64_t useful_by_shape[2];    /* useful pairs in tiles of each shape (BSATTN_SHAPE_*) */
+  int64_t physical_by_shape[2];  /* physical pairs in tiles of each shape */
+} bsattn_stats;
+
+/* Canonical plan arrays (views into plan memory, valid until bsattn_plan_destroy).
+ * Pages are ordered by K block then page; a page id indexes page_*.  Q tiles are
+ * ordered by Q block then row.  pl_ptr/pl_pages give each (unit, Q block) row's page
+ * ids: selected blocks ascending, each block's pages ascending. */
+typedef struct bsattn_plan_view {
+  int64_t n_pages;
+  const int32_t* page_kblock;
+  const int32_t* page_slot0;  /* first slot of the page in the K layout */
+  const int32_t* page_nvalid; /* 1..16 */
+  int64_t n_qtiles;
+  const int32_t* qt_qblock;
+  const int32_t* qt_row0;     /* first slot of the tile in the Q layout */
+  const int32_t* qt_rows;     /* valid rows */
+  const int32_t* qt_shape;    /* BSATTN_SHAPE_* */
+  int64_t n_rows;             /* n_units * n_qblocks */
+  const int64_t* pl_ptr;      /* [n_rows + 1] */
+  const int32_t* pl_pages;    /* [pl_ptr[n_rows]] */
+} bsattn_plan_view;
+
+typedef struct bsattn_plan bsattn_plan;
+
+/* Build a plan on the host: validate, cut K blocks into pages, route Q blocks into
+ * tiles, build the page lists and the pair counts.  page_size must be 16.  On success
+ * *out owns a new plan (free it with bsattn_plan_destroy); on failure *out is NULL. */
+int bsattn_plan_create(const bsattn_problem* problem, const bsattn_layout* q_layout,
+                       const bsattn_layout* k_layout, const bsattn_selection* selection,
+                       int32_t page_size, bsattn_plan** out);
+
+/* Bytes of device memory the plan needs (a multiple of 256). */
+int bsattn_plan_device_bytes(const bsattn_plan* plan, size_t* bytes);
+
+/* Copy the plan's device tables into dev (caller-owned device memory of at least
+ * bsattn_plan_device_bytes bytes, 256-byte aligned) on stream, asynchronously.  The
+ * host copy stays valid; dev must stay alive while the plan is used.  Uploading again
+ * rebinds the plan to the new buffer. */
+int bsattn_plan_upload(bsattn_plan* plan, void* dev, size_t bytes, void* stream);
+
+int bsattn_plan_stats(const bsattn_plan* plan, bsattn_stats* stats);
+
+int bsattn_plan_export(const bsattn_plan* plan, bsattn_plan_view* view);
+
+/* The forward pass: O and LSE for every (batch, query, head), asynchronously on stream.
+ * q, k, v, o: device bf16 tensors laid out as the problem's strides say (16-byte aligned
+ * rows); lse: device float32 [B, Hq, Nq]; scale: the softmax scale, finite and > 0.  Every
+ * O row and LSE entry is written.  No allocation, no synchronisation.  Returns BSATTN_E_STATE when the plan was never
+ * uploaded, BSATTN_E_ARG on a null or misaligned pointer, BSATTN_E_HIP on a launch error. */
+int bsattn_fwd(const bsattn_plan* plan, const void* q, const void* k, const void* v, void* o,
+               float* lse, float scale, void* stream);
+
+/* The part of bsattn_fwd that covers the Q tiles of one shape (BSATTN_SHAPE_128x128 or
+ * BSATTN_SHAPE_64x256, KPage abstract sentence 3): one kernel launch on stream.  The two
+ * shapes write disjoint rows of O and LSE, so calling both -- in either order, on one
+ * stream or on two -- is the same as one bsattn_fwd call.  Same arguments, ownership
+ * and errors as bsattn_fwd; an unknown shape is BSATTN_E_ARG. */
+int bsattn_fwd_shape(const bsattn_plan* plan, int32_t shape, const void* q, const void* k, const void* v,
+                     void* o, float* lse, float scale, void* stream);
+
+int bsattn_plan_destroy(bsattn_plan* plan);
+
+const char* bsattn_status_string(int status);
+
+/* The hipError_t of the most recent BSATTN_E_HIP on this thread (0 if none). */
+int bsattn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSATTN_H_ */

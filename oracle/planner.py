@@ -57,6 +57,8 @@ class Plan:
     useful: int
     physical: int
     n_ktiles: int
+    useful_by_shape: tuple = (0, 0)
+    physical_by_shape: tuple = (0, 0)
 
     @property
     def n_pages(self) -> int:
@@ -116,7 +118,7 @@ def build_plan(B, Hq, Hkv, q_offsets, q_perm, k_offsets, k_perm, sel_nb, sel_nh,
     pl_ptr = np.asarray(pl_ptr, dtype=np.int64)
 
     # R6: physical capacity and K-tile count over every (batch, head)
-    physical = 0
+    physical = [0, 0]
     nkt = 0
     for b in range(B):
         for h in range(Hq):
@@ -126,14 +128,65 @@ def build_plan(B, Hq, Hkv, q_offsets, q_perm, k_offsets, k_perm, sel_nb, sel_nh,
                 npg = int(pl_ptr[row + 1] - pl_ptr[row])
                 kt = -(-npg // PAGES_PER_KTILE[qs[t]])
                 nkt += kt
-                physical += TILE_ROWS[qs[t]] * TILE_COLS[qs[t]] * kt
+                physical[qs[t]] += TILE_ROWS[qs[t]] * TILE_COLS[qs[t]] * kt
     useful = useful_pairs(q_offsets, q_perm, k_offsets, k_perm, B, Hq, Hkv, sel_nb, sel_nh,
                           sel_row_ptr, sel_kblk, causal, q_pos0)
+    # useful pairs split by the shape of the Q tile that holds the query
+    qshape = np.zeros(int(q_offsets[-1]), dtype=np.int64)
+    for t in range(len(qq)):
+        qshape[qr[t]:qr[t] + qn[t]] = qs[t]
+    useful_sh = [0, 0]
+    for sh in (0, 1):
+        if not np.any(qshape == sh):
+            continue
+        # the same count restricted to queries of this shape: blocks cut down to those slots
+        offs = np.asarray(q_offsets, dtype=np.int64)
+        keep = np.nonzero(qshape == sh)[0]
+        new_offs = np.searchsorted(keep, offs, side="left")
+        sub_perm = None if q_perm is None else np.asarray(q_perm, dtype=np.int64)[keep]
+        if sub_perm is None:
+            sub_perm = keep
+        useful_sh[sh] = _useful_subset(new_offs, sub_perm, k_offsets, k_perm, B, Hq, Hkv, sel_nb, sel_nh,
+                                       sel_row_ptr, sel_kblk, causal, q_pos0)
     i32 = lambda a: np.asarray(a, dtype=np.int32)  # noqa: E731
     return Plan(page_kblock=i32(pk), page_slot0=i32(ps), page_nvalid=i32(pn),
                 qt_qblock=i32(qq), qt_row0=i32(qr), qt_rows=i32(qn), qt_shape=i32(qs),
                 n_units=n_units, pl_ptr=pl_ptr, pl_pages=i32(pl),
-                useful=int(useful), physical=int(physical), n_ktiles=int(nkt))
+                useful=int(useful), physical=int(sum(physical)), n_ktiles=int(nkt),
+                useful_by_shape=tuple(int(x) for x in useful_sh), physical_by_shape=tuple(int(x) for x in physical))
+
+
+def _useful_subset(q_offsets, q_tokens, k_offsets, k_perm, B, Hq, Hkv, sel_nb, sel_nh, sel_row_ptr, sel_kblk,
+                   causal, q_pos0):
+    """Useful pairs of a subset of the query slots: ``q_offsets`` re-cut over the kept slots
+    and ``q_tokens`` their tokens (positions for the causal test)."""
+    nqb = len(q_offsets) - 1
+    nkb = len(k_offsets) - 1
+
+    def unit_pairs(u):
+        tot = 0
+        for qb in range(nqb):
+            toks = np.asarray(q_tokens[q_offsets[qb]:q_offsets[qb + 1]], dtype=np.int64)
+            if toks.size == 0:
+                continue
+            for kb in selected_blocks(sel_row_ptr, sel_kblk, u * nqb + qb, nkb):
+                sl = np.arange(k_offsets[kb], k_offsets[kb + 1], dtype=np.int64)
+                kt = sl if k_perm is None else np.asarray(k_perm, dtype=np.int64)[sl]
+                if not causal:
+                    tot += toks.size * kt.size
+                else:
+                    tot += int(np.sum(kt[None, :] <= (q_pos0 + toks)[:, None]))
+        return tot
+
+    per_unit = {}  # heads sharing a selection unit have the same count
+    total = 0
+    for b in range(B):
+        for h in range(Hq):
+            u = selection_unit(b, h, B, Hq, Hkv, sel_nb, sel_nh)
+            if u not in per_unit:
+                per_unit[u] = unit_pairs(u)
+            total += per_unit[u]
+    return total
 
 
 def build_plan_w(w) -> Plan:

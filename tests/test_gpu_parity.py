@@ -1,0 +1,176 @@
+"""GPU parity: libbsattn's forward pass against the float64 oracle (needs an MI355X).
+
+All calls go through the C ABI (``bsattn_plan_create`` / ``_upload`` / ``bsattn_fwd``)
+via the ctypes binding.  Outputs are NaN-poisoned before every launch so unwritten rows
+show up.  Bar: O max-abs <= 2e-2 and mean-abs <= 1e-3, LSE max-abs <= 1e-3 for rows with
+keys; rows without keys must give O = 0 and LSE = -inf exactly.  Small cases compare
+every output; the full-size workloads compare sampled rows in the same launch
+configuration the benchmark times.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_fwd_amd as bs
+from oracle.attention import masked_attention_w
+from oracle.planner import build_plan_w
+from workloads.configs import make, make_random, make_chunk_gqa
+
+pytestmark = pytest.mark.gpu
+
+O_MAX, O_MEAN, LSE_MAX = 2e-2, 1e-3, 1e-3
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def run_gpu(w, plan=None, poison=True):
+    if plan is None:
+        plan = bs.Plan.from_workload(w).upload()
+    q, k, v = _dev(w.q), _dev(w.k), _dev(w.v)
+    o = torch.empty((w.B, w.Nq, w.Hq, w.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
+    if poison:
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+    plan.fwd(q, k, v, o, lse, scale=w.scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), plan
+
+
+def check_rows(o_gpu, l_gpu, o_ref, l_ref, label=""):
+    """o_*: [..., d] rows; l_*: matching LSE entries."""
+    assert np.all(np.isfinite(o_gpu)), f"{label}: non-finite O (unwritten rows?)"
+    live = np.isfinite(l_ref)
+    assert np.array_equal(np.isfinite(l_gpu), live), f"{label}: LSE finiteness differs"
+    assert np.all(l_gpu[~live] == -np.inf)
+    assert np.all(o_gpu[~live] == 0.0)
+    if live.any():
+        err = np.abs(o_gpu[live] - o_ref[live])
+        lerr = np.abs(l_gpu[live] - l_ref[live])
+        _say(f"{label}: O max {err.max():.3e} mean {err.mean():.3e}; LSE max {lerr.max():.3e}")
+        assert err.max() <= O_MAX, f"{label}: O max-abs {err.max()}"
+        assert err.mean() <= O_MEAN, f"{label}: O mean-abs {err.mean()}"
+        assert lerr.max() <= LSE_MAX, f"{label}: LSE max-abs {lerr.max()}"
+
+
+def check_full(w, label):
+    _say(f"[gpu] {label}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Nk={w.Nk} d={w.d} causal={w.causal}")
+    O, L, _ = run_gpu(w)
+    Or, Lr = masked_attention_w(w)
+    # O [B, Nq, Hq, d] -> rows aligned with LSE [B, Hq, Nq]
+    check_rows(np.transpose(O, (0, 2, 1, 3)), L, np.transpose(Or, (0, 2, 1, 3)), Lr, label)
+
+
+def check_sampled(w, label, heads, n_rows, seed=0, extra_rows=()):
+    _say(f"[gpu] {label}: B={w.B} Hq={w.Hq} Nq={w.Nq} Nk={w.Nk} d={w.d} sampled heads={list(heads)}")
+    O, L, _ = run_gpu(w)
+    assert np.all(np.isfinite(O)), f"{label}: unwritten or non-finite O"
+    rng = np.random.default_rng(seed)
+    req = []
+    for (b, h) in heads:
+        toks = np.unique(np.concatenate([rng.choice(w.Nq, n_rows, replace=False),
+                                         np.asarray(extra_rows, dtype=np.int64)])).astype(np.int64)
+        req.append((b, h, toks))
+    ref = masked_attention_w(w, rows=req)
+    for (b, h, toks), (o_ref, l_ref) in zip(req, ref):
+        check_rows(O[b, toks, h], L[b, h, toks], o_ref, l_ref, f"{label} b{b} h{h}")
+
+
+# ---------------------------------------------------------------------------
+# small cases: every output compared
+# ---------------------------------------------------------------------------
+def test_tiny_3d_full():
+    check_full(make(1), "tiny-3d")
+
+
+RANDOM_CASES = [
+    dict(seed=101, B=1, Hq=2, Hkv=2, Nq=700, Nk=900, d=128, max_qblock=300, max_kblock=100, sel_mode="head"),
+    dict(seed=102, B=1, Hq=2, Hkv=2, Nq=650, Nk=800, d=64, max_qblock=260, max_kblock=70, sel_mode="kv"),
+    dict(seed=103, B=2, Hq=4, Hkv=2, Nq=500, Nk=700, d=128, max_qblock=200, max_kblock=64, sel_mode="batch-kv",
+         use_perm=True),
+    dict(seed=104, B=1, Hq=4, Hkv=1, Nq=400, Nk=1100, d=128, max_qblock=400, max_kblock=64, sel_mode="shared",
+         causal=True),
+    dict(seed=105, B=1, Hq=2, Hkv=2, Nq=450, Nk=450, d=64, max_qblock=100, max_kblock=40, sel_mode="head",
+         causal=True, use_perm=True, allow_empty=True, density=0.3),
+    dict(seed=106, B=1, Hq=2, Hkv=1, Nq=333, Nk=517, d=128, max_qblock=64, max_kblock=17, sel_mode="kv",
+         allow_empty=True, density=0.1, unsorted=True, dup=True),
+    dict(seed=107, B=1, Hq=1, Hkv=1, Nq=129, Nk=257, d=128, max_qblock=129, max_kblock=257, sel_mode="shared",
+         density=1.0),
+    dict(seed=108, B=1, Hq=2, Hkv=2, Nq=64, Nk=16, d=64, max_qblock=64, max_kblock=16, sel_mode="head",
+         density=1.0),
+]
+
+
+@pytest.mark.parametrize("kw", RANDOM_CASES, ids=[f"seed{c['seed']}" for c in RANDOM_CASES])
+def test_random_full(kw):
+    check_full(make_random(**kw), f"random-{kw['seed']}")
+
+
+def test_empty_rows_and_empty_selection():
+    # no Q block selects anything: every row has no key
+    w = make_random(111, B=1, Hq=2, Hkv=2, Nq=200, Nk=300, d=128, max_qblock=90, max_kblock=50, sel_mode="head")
+    w.sel_row_ptr = np.zeros_like(w.sel_row_ptr)
+    w.sel_kblk = np.zeros(0, dtype=np.int32)
+    check_full(w, "empty-selection")
+
+
+def test_causal_rows_without_keys():
+    # queries positioned before every key: causal masking removes all their keys
+    w = make_random(112, B=1, Hq=2, Hkv=1, Nq=150, Nk=300, d=64, max_qblock=70, max_kblock=40, sel_mode="shared",
+                    causal=True, q_pos0=-100, density=0.8)
+    check_full(w, "causal-no-keys")
+
+
+def test_deterministic_bitwise():
+    w = make_random(113, B=1, Hq=4, Hkv=2, Nq=600, Nk=900, d=128, max_qblock=250, max_kblock=80, sel_mode="kv")
+    o1, l1, plan = run_gpu(w)
+    o2, l2, _ = run_gpu(w, plan=plan)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_plan_counts_match_oracle_plan():
+    w = make_random(114, B=2, Hq=4, Hkv=2, Nq=800, Nk=600, d=128, max_qblock=300, max_kblock=60,
+                    sel_mode="batch-kv", causal=True, use_perm=True, with_tensors=False)
+    st = bs.Plan.from_workload(w).stats
+    o = build_plan_w(w)
+    assert (st["useful"], st["physical"]) == (o.useful, o.physical)
+
+
+# ---------------------------------------------------------------------------
+# the benchmark workloads at full size
+# ---------------------------------------------------------------------------
+def test_onedim_full_size_sampled():
+    w = make(2)
+    check_sampled(w, "1d-8192", heads=[(0, 0), (0, 7), (0, 15)], n_rows=300, extra_rows=[0, 8191])
+
+
+def test_videodit_3d_full_size_sampled():
+    w = make(3)
+    # rows in full cubes, h-partial cubes (80 tokens), t-partial cubes (64, 40 tokens) and the last token
+    extra = [0, 127, 128 * 5, 128 * 5 + 79, 75600 - 1, 75600 - 40, 70000]
+    check_sampled(w, "videodit-3d", heads=[(0, 0), (0, 21), (0, 39)], n_rows=200, extra_rows=extra)
+
+
+def test_partitions_full_size_sampled():
+    w = make(4)
+    check_sampled(w, "indep-qk", heads=[(0, 0), (0, 39)], n_rows=200, extra_rows=[0, 75599])
+
+
+def test_chunk_gqa_scaled_full():
+    # same recipe as the long-context GQA workload, scaled down so every output is compared
+    w = make_chunk_gqa("chunk-gqa-small", 5, B=2, Hq=8, Hkv=2, d=128, Nk=64 * 96, Nq=256, chunk=64, topk=40)
+    check_full(w, "chunk-gqa-small")
+
+
+def test_chunk_gqa_full_size_sampled():
+    w = make(5)
+    check_sampled(w, "chunk-gqa", heads=[(0, 0), (1, 9), (3, 63)], n_rows=64, extra_rows=[0, 2047])

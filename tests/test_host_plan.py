@@ -1,0 +1,142 @@
+"""Host planner of libbsattn against the oracle's plan, bit for bit (CPU only; no GPU call).
+
+The planner is host C++ inside libbsattn.so; these tests create plans and read them
+back through the C ABI (bsattn_plan_create / _stats / _export) and compare every array
+and count with oracle.planner.  Nothing here launches a kernel.
+"""
+import ctypes
+import subprocess
+
+import numpy as np
+import pytest
+
+import block_sparse_attention_fwd_amd as bs
+from oracle.planner import build_plan_w
+from workloads.configs import make, make_random, make_chunk_gqa
+
+
+def _compare(w):
+    p = bs.Plan.from_workload(w)
+    ex = p.export()
+    st = p.stats
+    o = build_plan_w(w)
+    for name in ("page_kblock", "page_slot0", "page_nvalid", "qt_qblock", "qt_row0", "qt_rows", "qt_shape",
+                 "pl_ptr", "pl_pages"):
+        assert np.array_equal(ex[name], getattr(o, name)), name
+    assert st["useful"] == o.useful
+    assert st["physical"] == o.physical
+    assert st["n_ktiles"] == o.n_ktiles
+    assert st["n_pages"] == o.n_pages
+    assert (st["n_qtiles128"], st["n_qtiles64"]) == (o.n_qtiles128, o.n_qtiles64)
+    assert st["page_list_len"] == len(o.pl_pages)
+    assert tuple(st["physical_by_shape"]) == o.physical_by_shape
+    assert tuple(st["useful_by_shape"]) == o.useful_by_shape
+    assert sum(o.useful_by_shape) == o.useful
+    return st
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_configs_bit_exact(cfg):
+    _compare(make(cfg, with_tensors=False))
+
+
+def test_chunk_gqa_scaled_bit_exact():
+    w = make_chunk_gqa("small", 5, B=2, Hq=8, Hkv=2, d=64, Nk=64 * 300, Nq=512, chunk=64, topk=120)
+    st = _compare(w)
+    assert st["useful"] < 2 * 8 * 512 * 120 * 64  # causal exclusions removed
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_bit_exact(seed):
+    rng = np.random.default_rng(1000 + seed)
+    Hkv = int(rng.choice([1, 2]))
+    Hq = Hkv * int(rng.choice([1, 2, 4]))
+    kw = dict(B=int(rng.integers(1, 3)), Hq=Hq, Hkv=Hkv, Nq=int(rng.integers(1, 700)),
+              Nk=int(rng.integers(1, 700)), d=64, max_qblock=int(rng.integers(1, 300)),
+              max_kblock=int(rng.integers(1, 90)), density=float(rng.uniform(0.05, 0.9)),
+              sel_mode=str(rng.choice(["shared", "kv", "head", "batch-kv"])), allow_empty=bool(rng.random() < 0.4),
+              use_perm=bool(rng.random() < 0.4), causal=bool(rng.random() < 0.4), unsorted=bool(rng.random() < 0.3),
+              dup=bool(rng.random() < 0.3), with_tensors=False)
+    _compare(make_random(2000 + seed, **kw))
+
+
+def _problem(B=1, Hq=1, Hkv=1, Nq=4, Nk=4, d=64):
+    pr = bs.Problem()
+    pr.B, pr.Hq, pr.Hkv, pr.Nq, pr.Nk, pr.d = B, Hq, Hkv, Nq, Nk, d
+    pr.dtype = 1
+    return pr
+
+
+def _arr(x):
+    a = np.ascontiguousarray(x, dtype=np.int32)
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _status(pr, qo, ko, rp, kb, qperm=None, nb=1, nh=1, page=16):
+    keep = []
+
+    def p(x):
+        if x is None:
+            return None
+        a, ptr = _arr(x)
+        keep.append(a)
+        return ptr
+
+    ql = bs.Layout(len(qo) - 1, p(qo), p(qperm))
+    kl = bs.Layout(len(ko) - 1, p(ko), None)
+    sel = bs.Selection(nb, nh, p(rp), p(kb))
+    h = ctypes.c_void_p()
+    st = bs.library().bsattn_plan_create(ctypes.byref(pr), ctypes.byref(ql), ctypes.byref(kl), ctypes.byref(sel),
+                                         page, ctypes.byref(h))
+    if st == 0:
+        bs.library().bsattn_plan_destroy(h)
+    else:
+        assert not h.value
+    return st
+
+
+def test_error_statuses():
+    ok = dict(qo=[0, 4], ko=[0, 4], rp=[0, 1], kb=[0])
+    assert _status(_problem(), **ok) == 0
+    assert _status(_problem(d=96), **ok) == 4                    # head_dim
+    assert _status(_problem(), page=8, **ok) == 4                # page size
+    assert _status(_problem(Hq=3, Hkv=2), **ok) == 1             # Hq not a multiple of Hkv
+    assert _status(_problem(), qo=[0, 3], ko=[0, 4], rp=[0, 1], kb=[0]) == 2        # offsets end != Nq
+    assert _status(_problem(), qo=[0, 3, 2, 4], ko=[0, 4], rp=[0, 1, 1, 1], kb=[0]) == 2  # falling offsets
+    assert _status(_problem(), qperm=[0, 1, 1, 2], **ok) == 2    # not a permutation
+    assert _status(_problem(), qo=[0, 4], ko=[0, 4], rp=[0, 1], kb=[1]) == 3        # block id out of range
+    assert _status(_problem(), qo=[0, 4], ko=[0, 4], rp=[1, 1], kb=[0]) == 3        # row_ptr[0] != 0
+    assert _status(_problem(), qo=[0, 4], ko=[0, 4], rp=[0, 1], kb=[0], nh=3) == 3  # n_h not 1/Hkv/Hq
+    pr = _problem()
+    pr.dtype = 2
+    assert _status(pr, **ok) == 4
+    h = ctypes.c_void_p()
+    assert bs.library().bsattn_plan_create(None, None, None, None, 16, ctypes.byref(h)) == 1
+    assert bs.bsattn_status_string(3) == "invalid block selection"
+
+
+def test_fwd_before_upload_is_state_error():
+    w = make_random(3, Nq=40, Nk=40, d=64, with_tensors=False)
+    p = bs.Plan.from_workload(w)
+    with pytest.raises(bs.BsattnError) as e:
+        bs.bsattn_fwd(p.handle, 16, 16, 16, 16, 16, 0.125, 0)
+    assert e.value.status == 7
+    with pytest.raises(bs.BsattnError) as e:
+        bs.bsattn_plan_upload(p.handle, 0, 1 << 20, 0)
+    assert e.value.status == 1
+    with pytest.raises(bs.BsattnError) as e:
+        bs.bsattn_plan_upload(p.handle, 256, 1, 0)  # too small: rejected before any HIP call
+    assert e.value.status == 1
+
+
+def test_library_exports_every_declared_symbol():
+    import re
+    import os
+    hdr = open(os.path.join(os.path.dirname(bs.__file__), "..", "include", "bsattn.h")).read()
+    declared = sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(bsattn_\w+)\(", hdr, re.M)))
+    assert declared == sorted(bs.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", bs.LIB_PATH], capture_output=True, text=True).stdout
+    syms = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for name in declared:
+        assert name in syms, name
+        assert hasattr(bs.library(), name)
