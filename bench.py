@@ -63,6 +63,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=3, help="benchmark workload 1-5 (default 3: video-DiT 3D)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline sample budget (0 = skip)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB, 5 times (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
@@ -73,6 +75,16 @@ def main():
     import torch
     import block_sparse_attention_fwd_amd as bs
     from workloads.configs import make
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        a = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        c = torch.empty_like(a)
+        for _ in range(5):
+            c.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
+        return
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -108,6 +108,12 @@ int run_fwd(const bsattn_plan* plan, int sh0, int sh1, const void* q, const void
   };
   if (!aligned(q, pr.q_stride) || !aligned(o, pr.o_stride)) return BSATTN_E_ARG;
   if (pr.Nk > 0 && (!aligned(k, pr.k_stride) || !aligned(v, pr.v_stride))) return BSATTN_E_ARG;
+  for (const int64_t* st : {pr.q_stride, pr.k_stride, pr.v_stride, pr.o_stride})
+    if (st[0] < 0 || st[1] < 0 || st[2] < 0) return BSATTN_E_ARG;
+  // K/V rows of one (batch, KV head) are addressed with 32-bit byte offsets
+  const int64_t k_extent = pr.Nk > 0 ? (int64_t(pr.Nk) - 1) * pr.k_stride[1] * 2 + pr.d * 2 : 0;
+  const int64_t v_extent = pr.Nk > 0 ? (int64_t(pr.Nk) - 1) * pr.v_stride[1] * 2 + pr.d * 2 : 0;
+  if (k_extent > 0xffffffffLL || v_extent > 0xffffffffLL) return BSATTN_E_UNSUPPORTED;
 
   const uint8_t* base = static_cast<const uint8_t*>(plan->dev);
   bsattn::FwdParams fp{};
@@ -121,6 +127,10 @@ int run_fwd(const bsattn_plan* plan, int sh0, int sh1, const void* q, const void
   fp.qperm = plan->has_qperm ? reinterpret_cast<const int32_t*>(base + plan->off_qperm) : nullptr;
   fp.kperm = plan->has_kperm ? reinterpret_cast<const int32_t*>(base + plan->off_kperm) : nullptr;
   fp.q_pos0 = pr.q_pos0;
+  fp.k_extent = uint32_t(k_extent);
+  fp.v_extent = uint32_t(v_extent);
+  fp.k_sn_bytes = uint32_t(pr.k_stride[1] * 2);
+  fp.v_sn_bytes = uint32_t(pr.v_stride[1] * 2);
   fp.B = pr.B; fp.Hq = pr.Hq; fp.Hkv = pr.Hkv; fp.Nq = pr.Nq; fp.Nk = pr.Nk;
   fp.grp = pr.Hq / pr.Hkv;
   fp.nqb = plan->nqb;

@@ -18,6 +18,8 @@
 //   O^T += V^T P^T A = V^T read from LDS with ds_read_b64_tr_b16, B = P^T straight from
 //                  the score accumulators converted to bf16; the O^T accumulator again
 //                  gives each lane one query, so rescaling and the epilogue stay in-lane.
+// The exponentials of one 32-key block are followed by that block's P.V products, so the
+// matrix cores work while the next block's exponentials are computed.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -29,11 +31,11 @@ namespace bsattn {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
 #define GLB_AS __attribute__((address_space(1)))
+#define CONST_AS __attribute__((address_space(4)))
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
@@ -43,6 +45,16 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for LDS hand-off: publish this wave's LDS writes, then s_barrier.
+// Global->LDS loads are waited for explicitly (wait_vmcnt) before calling it.  The empty
+// asm statements keep the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), vmcnt/expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // XOR swizzle of the 16-byte chunk index inside an LDS row (d = 128: 16 chunks, d = 64:
@@ -59,37 +71,50 @@ __device__ __forceinline__ int swz(int row) {
   }
 }
 
-// Workgroup barrier for LDS hand-off: publish this wave's LDS writes, then s_barrier.
-// Global->LDS loads are waited for explicitly (wait_vmcnt) before calling it.  The empty
-// asm statements keep the compiler from moving memory accesses across the barrier.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), vmcnt/expcnt unconstrained
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
+// Lane l gets max / sum of its value and lane (l ^ 32)'s (v_permlane32_swap).
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ float wave_xor32(float x) {
-  return __shfl_xor(x, 32, 64);
+// Max / sum of 16 accumulator values as shallow trees (short dependency chains).
+__device__ __forceinline__ float max16(const f32x16& v) {
+  const float a = fmaxf(fmaxf(v[0], v[1]), v[2]), b2 = fmaxf(fmaxf(v[3], v[4]), v[5]);
+  const float c = fmaxf(fmaxf(v[6], v[7]), v[8]), d = fmaxf(fmaxf(v[9], v[10]), v[11]);
+  const float e = fmaxf(fmaxf(v[12], v[13]), v[14]);
+  return fmaxf(fmaxf(fmaxf(a, b2), c), fmaxf(fmaxf(d, e), v[15]));
+}
+__device__ __forceinline__ float sum16(const float* x) {
+  const float a = (x[0] + x[1]) + (x[2] + x[3]), b2 = (x[4] + x[5]) + (x[6] + x[7]);
+  const float c = (x[8] + x[9]) + (x[10] + x[11]), d = (x[12] + x[13]) + (x[14] + x[15]);
+  return (a + b2) + (c + d);
 }
 
 template <int D, int NRG, int NKG>
 struct Cfg {
-  static constexpr int kTileQ = 32 * NRG;
   static constexpr int kTileK = 128 * NKG;
   static constexpr int kPPT = kTileK / 16;           // pages per K tile
   static constexpr int kRowBytes = D * 2;
   static constexpr int kChunks = D / 8;              // 16-byte chunks per row
   static constexpr int kRowsPerInst = 64 / kChunks;  // rows per 64-lane 16-byte load
   static constexpr int kRowsPerWave = kTileK / 4;
+  static constexpr int kWavePages = kRowsPerWave / 16;
   static constexpr int kInst = kRowsPerWave / kRowsPerInst;  // loads per wave per tensor
   static constexpr int kBufBytes = kTileK * kRowBytes;
   static constexpr int kDS = D / 16;                 // k-steps of QK^T
   static constexpr int kDB = D / 32;                 // 32-wide d blocks of O^T
+  // two workgroups per CU when the LDS allows it
+  static constexpr int kWavesPerEU = (2 * kBufBytes + kTileK * 4) * 2 <= 160 * 1024 ? 2 : 1;
 };
 
-template <int D, int NRG, int NKG>
-__global__ void __launch_bounds__(256) fwd_kernel(FwdParams p) {
+template <int D, int NRG, int NKG, bool KPERM>
+__global__ void __launch_bounds__(256)
+    __attribute__((amdgpu_waves_per_eu(Cfg<D, NRG, NKG>::kWavesPerEU, Cfg<D, NRG, NKG>::kWavesPerEU)))
+    fwd_kernel(FwdParams p) {
   using C = Cfg<D, NRG, NKG>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem_k[C::kBufBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t smem_v[C::kBufBytes];
@@ -101,6 +126,11 @@ __global__ void __launch_bounds__(256) fwd_kernel(FwdParams p) {
   const int rg = wave % NRG;
   const int kg = wave / NRG;
   const int hh = lane >> 5;
+
+  // plan tables are read-only during the kernel: constant address space -> scalar loads
+  const CONST_AS int32_t* pl_ent = (const CONST_AS int32_t*)p.pl_ent;
+  const CONST_AS int32_t* pl_ptr = (const CONST_AS int32_t*)p.pl_ptr;
+  const CONST_AS int32_t* qtiles = (const CONST_AS int32_t*)p.qtiles;  // QTileDev records
 
   // ---- work item (XCD-aware: consecutive items share an XCD's L2) ----
   int work;
@@ -114,11 +144,17 @@ __global__ void __launch_bounds__(256) fwd_kernel(FwdParams p) {
   const int b = bh / p.Hq;
   const int h = bh - b * p.Hq;
   const int g = h / p.grp;
-  const QTileDev qt = p.qtiles[t];
+  struct {
+    int row0, rows, qblock;
+  } qt;
+  static_assert(sizeof(QTileDev) == 4 * sizeof(int32_t), "QTileDev layout");
+  qt.row0 = qtiles[4 * t];
+  qt.rows = qtiles[4 * t + 1];
+  qt.qblock = qtiles[4 * t + 2];
   const int unit = (b * p.ub_mul) * p.sel_nh + h / p.uh_div;
   const int row = unit * p.nqb + qt.qblock;
-  const int e0 = p.pl_ptr[row];
-  const int e1 = p.pl_ptr[row + 1];
+  const int e0 = pl_ptr[row];
+  const int e1 = pl_ptr[row + 1];
   const int nkt = (e1 - e0 + C::kPPT - 1) / C::kPPT;
 
   // ---- Q^T operand: lane holds query (lane % 32) of its row group, 8 d per k-step ----
@@ -139,69 +175,83 @@ __global__ void __launch_bounds__(256) fwd_kernel(FwdParams p) {
     const int64_t qp = p.q_pos0 + (int64_t)qtok;
     thr = qp < -1 ? -1 : (qp > 0x7ffffffe ? 0x7ffffffe : (int)qp);
   }
+  const int64_t minq_pos = p.q_pos0 + qt.row0 + rg * 32;  // smallest query position of the wave (identity Q layout)
 
-  // ---- loader: which rows this lane moves, and where ----
-  const int ld_lr = lane / C::kChunks;    // row inside one load
-  const int ld_pc = lane % C::kChunks;    // physical chunk slot this lane fills
-  const __bf16* kbase = reinterpret_cast<const __bf16*>(p.k) + (int64_t)b * p.k_sb + (int64_t)g * p.k_sh;
-  const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v) + (int64_t)b * p.v_sb + (int64_t)g * p.v_sh;
-  int ldtok[C::kInst];
+  // ---- loader: K/V pages -> LDS with buffer loads (SGPR base + 32-bit offsets) ----
+  // Row r of the tile goes to LDS row r; lane (ld_lr, ld_pc) of a load fills physical chunk
+  // ld_pc of row r, i.e. logical chunk ld_pc ^ swz(r).  The row's page is uniform per load.
+  const int ld_lr = lane / C::kChunks;  // row inside one load
+  const int ld_pc = lane % C::kChunks;  // physical chunk slot this lane fills
+  constexpr int kPeriod = 16 / C::kRowsPerInst;  // loads per 16-row page
+  const char* kslice = reinterpret_cast<const char*>(p.k) + ((int64_t)b * p.k_sb + (int64_t)g * p.k_sh) * 2;
+  const char* vslice = reinterpret_cast<const char*>(p.v) + ((int64_t)b * p.v_sb + (int64_t)g * p.v_sh) * 2;
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kslice, (short)0, p.k_extent, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)vslice, (short)0, p.v_extent, 0x00020000);
+  int ld_rip[kPeriod], ld_cb[kPeriod];  // row inside the page, logical chunk byte offset
+#pragma unroll
+  for (int n = 0; n < kPeriod; ++n) {
+    ld_rip[n] = (n * C::kRowsPerInst + ld_lr) & 15;
+    ld_cb[n] = (ld_pc ^ swz<D>(ld_rip[n])) * 16;
+  }
+  int ents[C::kWavePages];        // page entries of this wave's load rows (uniform)
+  int ldtok[KPERM ? C::kInst : 1];  // gathered key tokens (K permutation only)
 
-  // Tokens of the rows this lane loads for K tile kt (also published to ktok_lds, with
-  // empty slots marked), and whether this wave's 128-key slice of the tile needs masking.
-  // The page of every load instruction is wave-uniform: a 16-row page spans whole loads.
-  constexpr int kWavePages = C::kRowsPerWave / 16;
+  // Page entries / tokens of the rows this wave loads for K tile kt, the token list in
+  // ktok_lds (empty slots INT_MAX), and whether this wave's 128-key slice needs masking.
   auto fetch_tokens = [&](int kt) -> bool {
     const int etile = e0 + kt * C::kPPT;
-    int ents[kWavePages];
 #pragma unroll
-    for (int pp = 0; pp < kWavePages; ++pp) {
-      const int e = etile + wave * kWavePages + pp;
-      const int ent = p.pl_ent[e < e1 ? e : e1 - 1];
+    for (int pp = 0; pp < C::kWavePages; ++pp) {
+      const int e = etile + wave * C::kWavePages + pp;
+      const int ent = pl_ent[e < e1 ? e : e1 - 1];
       ents[pp] = e < e1 ? ent : 0;
     }
 #pragma unroll
     for (int n = 0; n < C::kInst; ++n) {
-      const int r = wave * C::kRowsPerWave + n * C::kRowsPerInst + ld_lr;
       const int ent = ents[(n * C::kRowsPerInst) >> 4];
-      const int nv = ent & 31;
-      const int rip = r & 15;
+      const int nv = ent & 31, rip = ld_rip[n % kPeriod];
       const int slot = (ent >> 5) + (rip < nv ? rip : 0);
-      ldtok[n] = p.kperm ? p.kperm[slot] : slot;
-    }
-#pragma unroll
-    for (int n = 0; n < C::kInst; ++n) {
-      const int r = wave * C::kRowsPerWave + n * C::kRowsPerInst + ld_lr;
-      const int nv = ents[(n * C::kRowsPerInst) >> 4] & 31;
-      if (ld_pc == 0) ktok_lds[r] = (r & 15) < nv ? ldtok[n] : 0x7fffffff;
+      int tok = slot;
+      if constexpr (KPERM) {
+        tok = p.kperm[slot];
+        ldtok[n] = tok;
+      }
+      if (ld_pc == 0) ktok_lds[wave * C::kRowsPerWave + n * C::kRowsPerInst + ld_lr] = rip < nv ? tok : 0x7fffffff;
     }
     bool need = false;
     int maxkey = -1;
 #pragma unroll
     for (int pp = 0; pp < 8; ++pp) {
       const int e = etile + kg * 8 + pp;
-      const int ent = p.pl_ent[e < e1 ? e : e1 - 1];
+      const int ent = pl_ent[e < e1 ? e : e1 - 1];
       const int nv = e < e1 ? (ent & 31) : 0;
       need |= nv < 16;
       const int last = (ent >> 5) + nv - 1;
       maxkey = (e < e1 && last > maxkey) ? last : maxkey;
     }
     if (p.causal) {
-      if (p.kperm || p.qperm)
+      if (KPERM || p.qperm)
         need = true;
       else
-        need |= (int64_t)maxkey > p.q_pos0 + qt.row0 + rg * 32;
+        need |= (int64_t)maxkey > minq_pos;
     }
     return need;
   };
-  auto issue = [&](const __bf16* base, int64_t sn, uint8_t* buf) {
+  auto issue = [&](const __amdgpu_buffer_rsrc_t& rsrc, uint32_t sn_bytes, uint8_t* buf) {
 #pragma unroll
     for (int n = 0; n < C::kInst; ++n) {
-      const int r = wave * C::kRowsPerWave + n * C::kRowsPerInst + ld_lr;
-      const int c = ld_pc ^ swz<D>(r);
-      const __bf16* src = base + (int64_t)ldtok[n] * sn + c * 8;
+      uint32_t voff, soff;
+      if constexpr (KPERM) {
+        voff = (uint32_t)ldtok[n] * sn_bytes + ld_cb[n % kPeriod];
+        soff = 0;
+      } else {
+        const int ent = ents[(n * C::kRowsPerInst) >> 4];
+        const int nv = ent & 31, rip = ld_rip[n % kPeriod];
+        voff = (rip < nv ? (uint32_t)rip * sn_bytes : 0u) + ld_cb[n % kPeriod];
+        soff = (uint32_t)(ent >> 5) * sn_bytes;
+      }
       uint8_t* dst = buf + (wave * C::kRowsPerWave + n * C::kRowsPerInst) * C::kRowBytes;
-      __builtin_amdgcn_global_load_lds((const GLB_AS void*)src, (LDS_AS void*)dst, 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)dst, 16, (int)voff, (int)soff, 0, 0);
     }
   };
 
@@ -214,12 +264,14 @@ __global__ void __launch_bounds__(256) fwd_kernel(FwdParams p) {
 
   const float sl2 = p.scale_log2;
   const int kbase_row = kg * 128;
+  // per-lane constants of the transposed V reads
+  const int v_rr = (lane & 15) >> 2, v_qq = lane & 3, v_dsub = (lane >> 4) & 1;
 
   bool nm_next = false;
   if (nkt > 0) {
     nm_next = fetch_tokens(0);
-    issue(kbase, p.k_sn, smem_k);
-    issue(vbase, p.v_sn, smem_v);
+    issue(krsrc, p.k_sn_bytes, smem_k);
+    issue(vrsrc, p.v_sn_bytes, smem_v);
   }
 
   for (int kt = 0; kt < nkt; ++kt) {
@@ -257,69 +309,65 @@ __global__ void __launch_bounds__(256) fwd_kernel(FwdParams p) {
       }
     }
 
-    // ---- online softmax ----
-    float mt = kNegInf;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[kb][e]);
-    mt = fmaxf(mt, wave_xor32(mt));
+    // ---- online softmax: tile max, rescale ----
+    float mt = fmaxf(fmaxf(max16(sacc[0]), max16(sacc[1])), fmaxf(max16(sacc[2]), max16(sacc[3])));
+    mt = xor32_max(mt);
     const float m_new = fmaxf(m_run, mt);
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * sl2);
     const float nb = -m_use * sl2;
-    float lsum = 0.f;
-    bf16x8 pb[8];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][e], sl2, nb));
-        lsum += pe;
-        pb[2 * kb + (e >> 3)][e & 7] = (__bf16)pe;
-      }
-    }
-    l_run = l_run * alpha + lsum;
     m_run = m_new;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
-    for (int db = 0; db < C::kDB; ++db) oacc[db] *= alpha;
+      for (int db = 0; db < C::kDB; ++db) oacc[db] *= alpha;
+    }
+    l_run *= alpha;
 
     wait_vmcnt<0>();  // V tile landed
     lds_barrier();    // every wave is done with the K buffer and the token list
     if (kt + 1 < nkt) {
       nm_next = fetch_tokens(kt + 1);
-      issue(kbase, p.k_sn, smem_k);
+      issue(krsrc, p.k_sn_bytes, smem_k);
     }
 
-    // ---- O^T += V^T P^T ----
-    {
-      const int G = lane >> 4, w16 = lane & 15, rr = w16 >> 2, qq = w16 & 3, dsub = G & 1;
+    // ---- per 32-key block: P = exp2(S*c - m*c), then O^T += V^T P^T ----
+    float lsum[4];
 #pragma unroll
-      for (int c16 = 0; c16 < 8; ++c16) {
-        const int key_a = kbase_row + 16 * c16 + 4 * hh + rr;
+    for (int kb = 0; kb < 4; ++kb) {
+      bf16x8 pb[2];
+      float pe[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][e], sl2, nb));
+        pb[e >> 3][e & 7] = (__bf16)pe[e];
+      }
+      lsum[kb] = sum16(pe);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int key_a = kbase_row + 32 * kb + 16 * half + 4 * hh + v_rr;
         const int key_b = key_a + 8;
 #pragma unroll
         for (int db = 0; db < C::kDB; ++db) {
-          const int lc = 4 * db + 2 * dsub + (qq >> 1);
-          const int off_in = (qq & 1) * 8;
-          const LDS_AS bf16x4* pa =
-              (const LDS_AS bf16x4*)(smem_v + key_a * C::kRowBytes + ((lc ^ swz<D>(key_a)) * 16) + off_in);
-          const LDS_AS bf16x4* pbp =
-              (const LDS_AS bf16x4*)(smem_v + key_b * C::kRowBytes + ((lc ^ swz<D>(key_b)) * 16) + off_in);
-          const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)pa);
-          const bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)pbp);
+          const int lc = 4 * db + 2 * v_dsub + (v_qq >> 1);
+          const int off_in = (v_qq & 1) * 8;
+          LDS_AS bf16x4* pa = (LDS_AS bf16x4*)(smem_v + key_a * C::kRowBytes + ((lc ^ swz<D>(key_a)) * 16) + off_in);
+          LDS_AS bf16x4* pv = (LDS_AS bf16x4*)(smem_v + key_b * C::kRowBytes + ((lc ^ swz<D>(key_b)) * 16) + off_in);
+          const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(pa);
+          const bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(pv);
           const bf16x8 av = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[c16], oacc[db], 0, 0, 0);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[half], oacc[db], 0, 0, 0);
         }
       }
     }
 
+    l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+
     lds_barrier();  // every wave is done with the V buffer
-    if (kt + 1 < nkt) issue(vbase, p.v_sn, smem_v);
+    if (kt + 1 < nkt) issue(vrsrc, p.v_sn_bytes, smem_v);
   }
 
   // ---- finish: combine lane halves, merge key groups, write O and LSE ----
-  float l_tot = l_run + wave_xor32(l_run);
+  float l_tot = xor32_sum(l_run);
   float m_fin = m_run;
   if constexpr (NKG == 2) {
     // key group 1 hands (m, l, O^T) to key group 0 through LDS (the K buffer is free)
@@ -371,7 +419,10 @@ __global__ void __launch_bounds__(256) fwd_kernel(FwdParams p) {
 template <int D, int NRG, int NKG>
 static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
   if (p.n_work <= 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_kernel<D, NRG, NKG>), dim3(p.n_work), dim3(256), 0, stream, p);
+  if (p.kperm)
+    hipLaunchKernelGGL((fwd_kernel<D, NRG, NKG, true>), dim3(p.n_work), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fwd_kernel<D, NRG, NKG, false>), dim3(p.n_work), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -29,6 +29,8 @@ struct FwdParams {
   const int32_t* qperm;       // slot -> token, or null
   const int32_t* kperm;
   int64_t q_pos0;
+  uint32_t k_extent, v_extent;  // bytes of one (batch, KV head) slice reachable from its base
+  uint32_t k_sn_bytes, v_sn_bytes;
   int32_t n_qtiles;           // tiles of this shape
   int32_t n_work;             // n_qtiles * B * Hq
   int32_t B, Hq, Hkv, Nq, Nk, grp;

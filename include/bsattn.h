@@ -153,7 +153,9 @@ int bsattn_plan_export(const bsattn_plan* plan, bsattn_plan_view* view);
 /* The forward pass: O and LSE for every (batch, query, head), asynchronously on stream.
  * q, k, v, o: device bf16 tensors laid out as the problem's strides say (16-byte aligned
  * rows); lse: device float32 [B, Hq, Nq]; scale: the softmax scale, finite and > 0.  Every
- * O row and LSE entry is written.  No allocation, no synchronisation.  Returns BSATTN_E_STATE when the plan was never
+ * O row and LSE entry is written.  No allocation, no synchronisation.  Strides must be
+ * non-negative, and the K (and V) rows of one (batch, KV head) must lie within 4 GiB of
+ * that slice's first element (BSATTN_E_UNSUPPORTED otherwise).  Returns BSATTN_E_STATE when the plan was never
  * uploaded, BSATTN_E_ARG on a null or misaligned pointer, BSATTN_E_HIP on a launch error. */
 int bsattn_fwd(const bsattn_plan* plan, const void* q, const void* k, const void* v, void* o,
                float* lse, float scale, void* stream);
