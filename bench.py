@@ -26,6 +26,29 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+SHORT_NAMES = {1: "tiny3d", 2: "onedim", 3: "videodit3d", 4: "partitions", 5: "chunkgqa"}
+KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_fwd_amd", "csrc", "fwd_kernel.hip")
+
+
+def measured_traffic(workload, shape_tag):
+    """HBM bytes per launch (read + write) recorded by rocprofv3 counter runs in
+    profiles/traffic_<workload>.txt -- only while the kernel source is the one measured."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{SHORT_NAMES.get(workload, '')}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            key, val = line.split("=", 1)
+            kv[key.strip()] = val.strip()
+    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if kv.get("source_sha256") != sha:
+        return None
+    try:
+        return int(kv[f"{shape_tag}.read_bytes"]) + int(kv[f"{shape_tag}.write_bytes"])
+    except KeyError:
+        return None
 
 
 def log(msg):
@@ -139,7 +162,7 @@ def main():
     u128 = st["useful_by_shape"][0]
     achieved = 4.0 * w.d * u128 / (k128 * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(args.workload, "128x128"),
                 "kernel": f"fwd_kernel<{w.d},4,1> (128x128 tiles)", "kernel_ms": round(k128, 4),
                 "useful_pairs_per_launch": u128}
 
