@@ -118,7 +118,7 @@ __global__ void __launch_bounds__(256)
   using C = Cfg<D, NRG, NKG>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem_k[C::kBufBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t smem_v[C::kBufBytes];
-  __shared__ int ktok_lds[C::kTileK];
+  __shared__ int ktok_lds[KPERM ? C::kTileK : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -187,36 +187,43 @@ __global__ void __launch_bounds__(256)
   const char* vslice = reinterpret_cast<const char*>(p.v) + ((int64_t)b * p.v_sb + (int64_t)g * p.v_sh) * 2;
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kslice, (short)0, p.k_extent, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)vslice, (short)0, p.v_extent, 0x00020000);
-  int ld_rip[kPeriod], ld_cb[kPeriod];  // row inside the page, logical chunk byte offset
+  int ld_rip[kPeriod], ld_cb[kPeriod];     // row inside the page, logical chunk byte offset
+  uint32_t ld_vk[kPeriod], ld_vv[kPeriod];  // per-lane K / V byte offsets of a full page's rows
 #pragma unroll
   for (int n = 0; n < kPeriod; ++n) {
     ld_rip[n] = (n * C::kRowsPerInst + ld_lr) & 15;
     ld_cb[n] = (ld_pc ^ swz<D>(ld_rip[n])) * 16;
+    ld_vk[n] = (uint32_t)ld_rip[n] * p.k_sn_bytes + ld_cb[n];
+    ld_vv[n] = (uint32_t)ld_rip[n] * p.v_sn_bytes + ld_cb[n];
   }
-  int ents[C::kWavePages];        // page entries of this wave's load rows (uniform)
+  int ents[C::kWavePages];          // page entries of this wave's load rows (uniform)
+  bool ents_full = true;            // all of them are full 16-row pages (uniform)
   int ldtok[KPERM ? C::kInst : 1];  // gathered key tokens (K permutation only)
+  int ment[8];                      // page entries of this wave's 128-key slice (uniform)
 
-  // Page entries / tokens of the rows this wave loads for K tile kt, the token list in
-  // ktok_lds (empty slots INT_MAX), and whether this wave's 128-key slice needs masking.
+  // Page entries (and, with a K permutation, tokens) of the rows this wave loads for K tile
+  // kt, and whether this wave's 128-key slice of that tile needs masking: a partial or empty
+  // page slot, or (causal) keys that may follow one of the wave's queries.  With a K
+  // permutation the slice's tokens also go to ktok_lds (empty slots INT_MAX).
   auto fetch_tokens = [&](int kt) -> bool {
     const int etile = e0 + kt * C::kPPT;
+    ents_full = true;
 #pragma unroll
     for (int pp = 0; pp < C::kWavePages; ++pp) {
       const int e = etile + wave * C::kWavePages + pp;
       const int ent = pl_ent[e < e1 ? e : e1 - 1];
       ents[pp] = e < e1 ? ent : 0;
+      ents_full &= (ents[pp] & 31) == 16;
     }
+    if constexpr (KPERM) {
 #pragma unroll
-    for (int n = 0; n < C::kInst; ++n) {
-      const int ent = ents[(n * C::kRowsPerInst) >> 4];
-      const int nv = ent & 31, rip = ld_rip[n % kPeriod];
-      const int slot = (ent >> 5) + (rip < nv ? rip : 0);
-      int tok = slot;
-      if constexpr (KPERM) {
-        tok = p.kperm[slot];
+      for (int n = 0; n < C::kInst; ++n) {
+        const int ent = ents[(n * C::kRowsPerInst) >> 4];
+        const int nv = ent & 31, rip = ld_rip[n % kPeriod];
+        const int tok = p.kperm[(ent >> 5) + (rip < nv ? rip : 0)];
         ldtok[n] = tok;
+        if (ld_pc == 0) ktok_lds[wave * C::kRowsPerWave + n * C::kRowsPerInst + ld_lr] = rip < nv ? tok : 0x7fffffff;
       }
-      if (ld_pc == 0) ktok_lds[wave * C::kRowsPerWave + n * C::kRowsPerInst + ld_lr] = rip < nv ? tok : 0x7fffffff;
     }
     bool need = false;
     int maxkey = -1;
@@ -224,10 +231,11 @@ __global__ void __launch_bounds__(256)
     for (int pp = 0; pp < 8; ++pp) {
       const int e = etile + kg * 8 + pp;
       const int ent = pl_ent[e < e1 ? e : e1 - 1];
-      const int nv = e < e1 ? (ent & 31) : 0;
+      ment[pp] = e < e1 ? ent : 0;
+      const int nv = ment[pp] & 31;
       need |= nv < 16;
-      const int last = (ent >> 5) + nv - 1;
-      maxkey = (e < e1 && last > maxkey) ? last : maxkey;
+      const int last = (ment[pp] >> 5) + nv - 1;
+      maxkey = (nv > 0 && last > maxkey) ? last : maxkey;
     }
     if (p.causal) {
       if (KPERM || p.qperm)
@@ -237,21 +245,33 @@ __global__ void __launch_bounds__(256)
     }
     return need;
   };
-  auto issue = [&](const __amdgpu_buffer_rsrc_t& rsrc, uint32_t sn_bytes, uint8_t* buf) {
+  // Loads of one tensor's rows for the tile whose entries fetch_tokens read.  Rows past a
+  // page's valid count (and empty page slots) load the page's first row / token 0: finite
+  // data that the mask removes.
+  auto issue = [&](const __amdgpu_buffer_rsrc_t& rsrc, uint32_t sn_bytes, const uint32_t (&vfull)[kPeriod],
+                   uint8_t* buf) {
+    if (KPERM || !ents_full) {
 #pragma unroll
-    for (int n = 0; n < C::kInst; ++n) {
-      uint32_t voff, soff;
-      if constexpr (KPERM) {
-        voff = (uint32_t)ldtok[n] * sn_bytes + ld_cb[n % kPeriod];
-        soff = 0;
-      } else {
-        const int ent = ents[(n * C::kRowsPerInst) >> 4];
-        const int nv = ent & 31, rip = ld_rip[n % kPeriod];
-        voff = (rip < nv ? (uint32_t)rip * sn_bytes : 0u) + ld_cb[n % kPeriod];
-        soff = (uint32_t)(ent >> 5) * sn_bytes;
+      for (int n = 0; n < C::kInst; ++n) {
+        uint32_t voff, soff;
+        if constexpr (KPERM) {
+          voff = (uint32_t)ldtok[n] * sn_bytes + ld_cb[n % kPeriod];
+          soff = 0;
+        } else {
+          const int ent = ents[(n * C::kRowsPerInst) >> 4];
+          voff = ld_rip[n % kPeriod] < (ent & 31) ? vfull[n % kPeriod] : (uint32_t)ld_cb[n % kPeriod];
+          soff = (uint32_t)(ent >> 5) * sn_bytes;
+        }
+        uint8_t* dst = buf + (wave * C::kRowsPerWave + n * C::kRowsPerInst) * C::kRowBytes;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)dst, 16, (int)voff, (int)soff, 0, 0);
       }
-      uint8_t* dst = buf + (wave * C::kRowsPerWave + n * C::kRowsPerInst) * C::kRowBytes;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)dst, 16, (int)voff, (int)soff, 0, 0);
+    } else {
+#pragma unroll
+      for (int n = 0; n < C::kInst; ++n) {
+        const uint32_t soff = (uint32_t)(ents[(n * C::kRowsPerInst) >> 4] >> 5) * sn_bytes;
+        uint8_t* dst = buf + (wave * C::kRowsPerWave + n * C::kRowsPerInst) * C::kRowBytes;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)dst, 16, (int)vfull[n % kPeriod], (int)soff, 0, 0);
+      }
     }
   };
 
@@ -270,8 +290,8 @@ __global__ void __launch_bounds__(256)
   bool nm_next = false;
   if (nkt > 0) {
     nm_next = fetch_tokens(0);
-    issue(krsrc, p.k_sn_bytes, smem_k);
-    issue(vrsrc, p.v_sn_bytes, smem_v);
+    issue(krsrc, p.k_sn_bytes, ld_vk, smem_k);
+    issue(vrsrc, p.v_sn_bytes, ld_vv, smem_v);
   }
 
   for (int kt = 0; kt < nkt; ++kt) {
@@ -301,10 +321,21 @@ __global__ void __launch_bounds__(256)
       for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const i32x4 kt4 = *reinterpret_cast<const i32x4*>(&ktok_lds[kbase_row + 32 * kb + 8 * i + 4 * hh]);
+          if constexpr (KPERM) {
+            const i32x4 t4 = *reinterpret_cast<const i32x4*>(&ktok_lds[kbase_row + 32 * kb + 8 * i + 4 * hh]);
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (kt4[j] > thr) sacc[kb][4 * i + j] = kNegInf;
+            for (int j = 0; j < 4; ++j)
+              if (t4[j] > thr) sacc[kb][4 * i + j] = kNegInf;
+          } else {
+            // key 32kb + 8i + 4hh + j is row 8(i&1) + 4hh + j of page 2kb + i/2
+            const int ent = ment[2 * kb + (i >> 1)];
+            int lim = (ent & 31) - 1;
+            if (p.causal) lim = min(lim, thr - (ent >> 5));
+            const int rip0 = 8 * (i & 1) + 4 * hh;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (rip0 + j > lim) sacc[kb][4 * i + j] = kNegInf;
+          }
         }
       }
     }
@@ -327,7 +358,7 @@ __global__ void __launch_bounds__(256)
     lds_barrier();    // every wave is done with the K buffer and the token list
     if (kt + 1 < nkt) {
       nm_next = fetch_tokens(kt + 1);
-      issue(krsrc, p.k_sn_bytes, smem_k);
+      issue(krsrc, p.k_sn_bytes, ld_vk, smem_k);
     }
 
     // ---- per 32-key block: P = exp2(S*c - m*c), then O^T += V^T P^T ----
@@ -363,7 +394,7 @@ __global__ void __launch_bounds__(256)
     l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
 
     lds_barrier();  // every wave is done with the V buffer
-    if (kt + 1 < nkt) issue(vrsrc, p.v_sn_bytes, smem_v);
+    if (kt + 1 < nkt) issue(vrsrc, p.v_sn_bytes, ld_vv, smem_v);
   }
 
   // ---- finish: combine lane halves, merge key groups, write O and LSE ----
