@@ -32,6 +32,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+// N consecutive dwords with dword alignment: one scalar load (s_load_dwordxN) when uniform
+template <int N>
+using SVec = int __attribute__((ext_vector_type(N), aligned(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
 #define GLB_AS __attribute__((address_space(1)))
@@ -94,10 +97,10 @@ __device__ __forceinline__ float sum16(const float* x) {
   return (a + b2) + (c + d);
 }
 
-template <int D, int NRG, int NKG>
+template <int D, int NRG, int NKG, int KB>
 struct Cfg {
-  static constexpr int kTileK = 128 * NKG;
-  static constexpr int kPPT = kTileK / 16;           // pages per K tile
+  static constexpr int kTileK = 32 * KB * NKG;       // keys per pipeline stage (LDS tile)
+  static constexpr int kPPT = kTileK / 16;           // pages per stage
   static constexpr int kRowBytes = D * 2;
   static constexpr int kChunks = D / 8;              // 16-byte chunks per row
   static constexpr int kRowsPerInst = 64 / kChunks;  // rows per 64-lane 16-byte load
@@ -108,16 +111,27 @@ struct Cfg {
   static constexpr int kDS = D / 16;                 // k-steps of QK^T
   static constexpr int kDB = D / 32;                 // 32-wide d blocks of O^T
   // two workgroups per CU when the LDS allows it
-  static constexpr int kWavesPerEU = (2 * kBufBytes + kTileK * 4) * 2 <= 160 * 1024 ? 2 : 1;
+  // workgroups per CU that the LDS allows (at most 3: the register budget of 168)
+  static constexpr int kLds = 2 * kBufBytes + kTileK * 4;
+#ifdef BSATTN_WPE_MAX
+  static constexpr int kWpeMax = BSATTN_WPE_MAX;
+#else
+  static constexpr int kWpeMax = 2;  // three waves per SIMD would leave 168 VGPRs: too few
+#endif
+  static constexpr int kWavesPerEU =
+      (kWpeMax >= 3 && 3 * kLds <= 160 * 1024) ? 3 : ((kWpeMax >= 2 && 2 * kLds <= 160 * 1024) ? 2 : 1);
 };
 
-template <int D, int NRG, int NKG, bool KPERM>
+template <int D, int NRG, int NKG, int KB, bool KPERM>
 __global__ void __launch_bounds__(256)
-    __attribute__((amdgpu_waves_per_eu(Cfg<D, NRG, NKG>::kWavesPerEU, Cfg<D, NRG, NKG>::kWavesPerEU)))
+    __attribute__((amdgpu_waves_per_eu(Cfg<D, NRG, NKG, KB>::kWavesPerEU, Cfg<D, NRG, NKG, KB>::kWavesPerEU)))
     fwd_kernel(FwdParams p) {
-  using C = Cfg<D, NRG, NKG>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem_k[C::kBufBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t smem_v[C::kBufBytes];
+  using C = Cfg<D, NRG, NKG, KB>;
+  // K tile, then V tile; after the last tile the whole array holds the key-group merge
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::kBufBytes];
+  uint8_t* const smem_k = smem;
+  uint8_t* const smem_v = smem + C::kBufBytes;
+  static_assert(NKG == 1 || NRG * (C::kDB * 16 + 2) * 64 * 4 <= 2 * C::kBufBytes, "merge buffer fits");
   __shared__ int ktok_lds[KPERM ? C::kTileK : 4];
 
   const int tid = threadIdx.x;
@@ -199,20 +213,24 @@ __global__ void __launch_bounds__(256)
   int ents[C::kWavePages];          // page entries of this wave's load rows (uniform)
   bool ents_full = true;            // all of them are full 16-row pages (uniform)
   int ldtok[KPERM ? C::kInst : 1];  // gathered key tokens (K permutation only)
-  int ment[8];                      // page entries of this wave's 128-key slice (uniform)
+  int ment[2 * KB];                 // page entries of this wave's key slice (uniform)
 
   // Page entries (and, with a K permutation, tokens) of the rows this wave loads for K tile
   // kt, and whether this wave's 128-key slice of that tile needs masking: a partial or empty
   // page slot, or (causal) keys that may follow one of the wave's queries.  With a K
   // permutation the slice's tokens also go to ktok_lds (empty slots INT_MAX).
   auto fetch_tokens = [&](int kt) -> bool {
+    // two scalar vector loads: the wave's load pages and its key slice (the entry array is
+    // zero-padded, so reading past a list's end stays in bounds; those slots count as empty)
     const int etile = e0 + kt * C::kPPT;
+    const int el = etile + wave * C::kWavePages;
+    const int es = etile + kg * 2 * KB;
+    const SVec<C::kWavePages> lv = *(const CONST_AS SVec<C::kWavePages>*)(pl_ent + el);
+    const SVec<2 * KB> sv = *(const CONST_AS SVec<2 * KB>*)(pl_ent + es);
     ents_full = true;
 #pragma unroll
     for (int pp = 0; pp < C::kWavePages; ++pp) {
-      const int e = etile + wave * C::kWavePages + pp;
-      const int ent = pl_ent[e < e1 ? e : e1 - 1];
-      ents[pp] = e < e1 ? ent : 0;
+      ents[pp] = el + pp < e1 ? lv[pp] : 0;
       ents_full &= (ents[pp] & 31) == 16;
     }
     if constexpr (KPERM) {
@@ -228,10 +246,8 @@ __global__ void __launch_bounds__(256)
     bool need = false;
     int maxkey = -1;
 #pragma unroll
-    for (int pp = 0; pp < 8; ++pp) {
-      const int e = etile + kg * 8 + pp;
-      const int ent = pl_ent[e < e1 ? e : e1 - 1];
-      ment[pp] = e < e1 ? ent : 0;
+    for (int pp = 0; pp < 2 * KB; ++pp) {
+      ment[pp] = es + pp < e1 ? sv[pp] : 0;
       const int nv = ment[pp] & 31;
       need |= nv < 16;
       const int last = (ment[pp] >> 5) + nv - 1;
@@ -283,7 +299,7 @@ __global__ void __launch_bounds__(256)
   for (int db = 0; db < C::kDB; ++db) oacc[db] = f32x16{};
 
   const float sl2 = p.scale_log2;
-  const int kbase_row = kg * 128;
+  const int kbase_row = kg * 32 * KB;
   // per-lane constants of the transposed V reads
   const int v_rr = (lane & 15) >> 2, v_qq = lane & 3, v_dsub = (lane >> 4) & 1;
 
@@ -301,13 +317,13 @@ __global__ void __launch_bounds__(256)
     lds_barrier();
 
     // ---- S^T = K Q^T ----
-    f32x16 sacc[4];
+    f32x16 sacc[KB];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) sacc[kb] = f32x16{};
+    for (int kb = 0; kb < KB; ++kb) sacc[kb] = f32x16{};
 #pragma unroll
     for (int s = 0; s < C::kDS; ++s) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
         const int r = kbase_row + 32 * kb + (lane & 31);
         const int c = (2 * s + hh) ^ swz<D>(r);
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(smem_k + r * C::kRowBytes + c * 16);
@@ -318,7 +334,7 @@ __global__ void __launch_bounds__(256)
     // ---- exact mask: empty page slots, causally hidden keys ----
     if (need_mask) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if constexpr (KPERM) {
@@ -341,7 +357,8 @@ __global__ void __launch_bounds__(256)
     }
 
     // ---- online softmax: tile max, rescale ----
-    float mt = fmaxf(fmaxf(max16(sacc[0]), max16(sacc[1])), fmaxf(max16(sacc[2]), max16(sacc[3])));
+    float mt = fmaxf(max16(sacc[0]), max16(sacc[1]));
+    if constexpr (KB == 4) mt = fmaxf(mt, fmaxf(max16(sacc[2]), max16(sacc[3])));
     mt = xor32_max(mt);
     const float m_new = fmaxf(m_run, mt);
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
@@ -362,9 +379,9 @@ __global__ void __launch_bounds__(256)
     }
 
     // ---- per 32-key block: P = exp2(S*c - m*c), then O^T += V^T P^T ----
-    float lsum[4];
+    float lsum[KB];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
       bf16x8 pb[2];
       float pe[16];
 #pragma unroll
@@ -391,7 +408,10 @@ __global__ void __launch_bounds__(256)
       }
     }
 
-    l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+    if constexpr (KB == 4)
+      l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+    else
+      l_run += lsum[0] + lsum[1];
 
     lds_barrier();  // every wave is done with the V buffer
     if (kt + 1 < nkt) issue(vrsrc, p.v_sn_bytes, ld_vv, smem_v);
@@ -403,7 +423,7 @@ __global__ void __launch_bounds__(256)
   if constexpr (NKG == 2) {
     // key group 1 hands (m, l, O^T) to key group 0 through LDS (the K buffer is free)
     __syncthreads();
-    float* mb = reinterpret_cast<float*>(smem_k) + rg * (C::kDB * 16 + 2) * 64;
+    float* mb = reinterpret_cast<float*>(smem) + rg * (C::kDB * 16 + 2) * 64;
     if (kg == 1) {
 #pragma unroll
       for (int db = 0; db < C::kDB; ++db)
@@ -447,19 +467,27 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-template <int D, int NRG, int NKG>
+template <int D, int NRG, int NKG, int KB>
 static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
   if (p.n_work <= 0) return hipSuccess;
   if (p.kperm)
-    hipLaunchKernelGGL((fwd_kernel<D, NRG, NKG, true>), dim3(p.n_work), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<D, NRG, NKG, KB, true>), dim3(p.n_work), dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((fwd_kernel<D, NRG, NKG, false>), dim3(p.n_work), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<D, NRG, NKG, KB, false>), dim3(p.n_work), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
+#ifndef BSATTN_KB128
+#define BSATTN_KB128 4
+#endif
+#ifndef BSATTN_KB64
+#define BSATTN_KB64 2
+#endif
+
 hipError_t launch_fwd_shape(const FwdParams& p, int shape, int d, hipStream_t stream) {
-  if (d == 128) return shape == 0 ? launch_one<128, 4, 1>(p, stream) : launch_one<128, 2, 2>(p, stream);
-  return shape == 0 ? launch_one<64, 4, 1>(p, stream) : launch_one<64, 2, 2>(p, stream);
+  if (d == 128)
+    return shape == 0 ? launch_one<128, 4, 1, BSATTN_KB128>(p, stream) : launch_one<128, 2, 2, BSATTN_KB64>(p, stream);
+  return shape == 0 ? launch_one<64, 4, 1, BSATTN_KB128>(p, stream) : launch_one<64, 2, 2, BSATTN_KB64>(p, stream);
 }
 
 }  // namespace bsattn

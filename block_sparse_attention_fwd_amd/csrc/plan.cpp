@@ -208,7 +208,8 @@ int build_plan(const bsattn_problem& prob, const bsattn_layout& ql, const bsattn
   p->off_plptr = off;
   off = align256(off + sizeof(int32_t) * (size_t(n_rows) + 1));
   p->off_plent = off;
-  off = align256(off + sizeof(int32_t) * p->pl_pages.size());
+  // zero padding past the last entry: the kernel reads whole K tiles of entries at once
+  off = align256(off + sizeof(int32_t) * (p->pl_pages.size() + kEntryPad));
   p->has_qperm = ql.perm != nullptr;
   p->has_kperm = kl.perm != nullptr;
   p->off_qperm = off;
