@@ -127,11 +127,12 @@ __global__ void __launch_bounds__(256)
     __attribute__((amdgpu_waves_per_eu(Cfg<D, NRG, NKG, KB>::kWavesPerEU, Cfg<D, NRG, NKG, KB>::kWavesPerEU)))
     fwd_kernel(FwdParams p) {
   using C = Cfg<D, NRG, NKG, KB>;
-  // K tile, then V tile; after the last tile the whole array holds the key-group merge
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::kBufBytes];
-  uint8_t* const smem_k = smem;
-  uint8_t* const smem_v = smem + C::kBufBytes;
-  static_assert(NKG == 1 || NRG * (C::kDB * 16 + 2) * 64 * 4 <= 2 * C::kBufBytes, "merge buffer fits");
+  // K and V tiles as separate objects: the compiler can then tell that reads of one never
+  // touch the other's in-flight loads and adds no waits of its own.  After the last tile the
+  // two arrays hold the key-group merge (row group 0 in K, row group 1 in V).
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_k[C::kBufBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_v[C::kBufBytes];
+  static_assert(NKG == 1 || (NRG <= 2 && (C::kDB * 16 + 2) * 64 * 4 <= C::kBufBytes), "merge buffer fits");
   __shared__ int ktok_lds[KPERM ? C::kTileK : 4];
 
   const int tid = threadIdx.x;
@@ -423,7 +424,7 @@ __global__ void __launch_bounds__(256)
   if constexpr (NKG == 2) {
     // key group 1 hands (m, l, O^T) to key group 0 through LDS (the K buffer is free)
     __syncthreads();
-    float* mb = reinterpret_cast<float*>(smem) + rg * (C::kDB * 16 + 2) * 64;
+    float* mb = reinterpret_cast<float*>(rg == 0 ? smem_k : smem_v);
     if (kg == 1) {
 #pragma unroll
       for (int db = 0; db < C::kDB; ++db)
