@@ -41,6 +41,34 @@ using SVec = int __attribute__((ext_vector_type(N), aligned(4)));
 #define CONST_AS __attribute__((address_space(4)))
 
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLn2 = 0.693147180559945309f;
+
+// Ties a register value to this point of the program: an empty asm statement that uses it.
+// Device pass only (the host pass instantiates kernels for their launch stubs, and "v" names
+// no host register class).
+template <typename T>
+__device__ __forceinline__ void pin(const T& x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" ::"v"(x));
+#endif
+}
+
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+template <int I>
+struct IntTag {
+  static constexpr int value = I;
+};
+// f(IntTag<I>{}) for I = B .. E - 1, unrolled at compile time
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(IntTag<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
 // lgkmcnt[11:8] | vmcnt_hi[15:14]).
@@ -264,31 +292,27 @@ __global__ void __launch_bounds__(256)
   };
   // Loads of one tensor's rows for the tile whose entries fetch_tokens read.  Rows past a
   // page's valid count (and empty page slots) load the page's first row / token 0: finite
-  // data that the mask removes.
+  // data that the mask removes.  Only the per-lane offsets depend on whether every page is
+  // full; the loads themselves are issued unconditionally, so the compiler can count them.
   auto issue = [&](const __amdgpu_buffer_rsrc_t& rsrc, uint32_t sn_bytes, const uint32_t (&vfull)[kPeriod],
                    uint8_t* buf) {
-    if (KPERM || !ents_full) {
+    uint32_t voff[C::kInst], soff[C::kInst];
 #pragma unroll
-      for (int n = 0; n < C::kInst; ++n) {
-        uint32_t voff, soff;
-        if constexpr (KPERM) {
-          voff = (uint32_t)ldtok[n] * sn_bytes + ld_cb[n % kPeriod];
-          soff = 0;
-        } else {
-          const int ent = ents[(n * C::kRowsPerInst) >> 4];
-          voff = ld_rip[n % kPeriod] < (ent & 31) ? vfull[n % kPeriod] : (uint32_t)ld_cb[n % kPeriod];
-          soff = (uint32_t)(ent >> 5) * sn_bytes;
-        }
-        uint8_t* dst = buf + (wave * C::kRowsPerWave + n * C::kRowsPerInst) * C::kRowBytes;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)dst, 16, (int)voff, (int)soff, 0, 0);
+    for (int n = 0; n < C::kInst; ++n) {
+      if constexpr (KPERM) {
+        voff[n] = (uint32_t)ldtok[n] * sn_bytes + ld_cb[n % kPeriod];
+        soff[n] = 0;
+      } else {
+        const int ent = ents[(n * C::kRowsPerInst) >> 4];
+        voff[n] = vfull[n % kPeriod];
+        if (!ents_full && ld_rip[n % kPeriod] >= (ent & 31)) voff[n] = (uint32_t)ld_cb[n % kPeriod];
+        soff[n] = (uint32_t)(ent >> 5) * sn_bytes;
       }
-    } else {
+    }
 #pragma unroll
-      for (int n = 0; n < C::kInst; ++n) {
-        const uint32_t soff = (uint32_t)(ents[(n * C::kRowsPerInst) >> 4] >> 5) * sn_bytes;
-        uint8_t* dst = buf + (wave * C::kRowsPerWave + n * C::kRowsPerInst) * C::kRowBytes;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)dst, 16, (int)vfull[n % kPeriod], (int)soff, 0, 0);
-      }
+    for (int n = 0; n < C::kInst; ++n) {
+      uint8_t* dst = buf + (wave * C::kRowsPerWave + n * C::kRowsPerInst) * C::kRowBytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)dst, 16, (int)voff[n], (int)soff[n], 0, 0);
     }
   };
 
@@ -311,7 +335,12 @@ __global__ void __launch_bounds__(256)
     issue(vrsrc, p.v_sn_bytes, ld_vv, smem_v);
   }
 
-  for (int kt = 0; kt < nkt; ++kt) {
+  // One K tile.  MORE: a next tile exists and its loads are issued here.  The last tile is
+  // a separate instantiation so that, inside the loop, the loads are unconditional: the
+  // compiler then sees that the K tile at the loop head is older than the V tile behind it
+  // and waits for the K loads only, instead of for every load in flight.
+  auto tile = [&](int kt, auto more_tag) __attribute__((always_inline)) {
+    constexpr bool MORE = decltype(more_tag)::value;
     const bool need_mask = nm_next;
 
     wait_vmcnt<C::kInst>();  // K tile landed (V may still be in flight)
@@ -374,7 +403,7 @@ __global__ void __launch_bounds__(256)
 
     wait_vmcnt<0>();  // V tile landed
     lds_barrier();    // every wave is done with the K buffer and the token list
-    if (kt + 1 < nkt) {
+    if constexpr (MORE) {
       nm_next = fetch_tokens(kt + 1);
       issue(krsrc, p.k_sn_bytes, ld_vk, smem_k);
     }
@@ -414,9 +443,13 @@ __global__ void __launch_bounds__(256)
     else
       l_run += lsum[0] + lsum[1];
 
-    lds_barrier();  // every wave is done with the V buffer
-    if (kt + 1 < nkt) issue(vrsrc, p.v_sn_bytes, ld_vv, smem_v);
-  }
+    if constexpr (MORE) {
+      lds_barrier();  // every wave is done with the V buffer
+      issue(vrsrc, p.v_sn_bytes, ld_vv, smem_v);
+    }
+  };
+  for (int kt = 0; kt + 1 < nkt; ++kt) tile(kt, BoolTag<true>{});
+  if (nkt > 0) tile(nkt - 1, BoolTag<false>{});
 
   // ---- finish: combine lane halves, merge key groups, write O and LSE ----
   float l_tot = xor32_sum(l_run);
@@ -468,6 +501,488 @@ __global__ void __launch_bounds__(256)
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// 128x128 tiles in ping-pong: 8 waves, two per SIMD.  Waves 0-3 (group 0) and 4-7 (group 1)
+// each hold the tile's four row groups of 32 queries and split its 64-key stages (4 pages):
+// group g takes stages g, g + 2, g + 4, ...  The walk alternates two kinds of phase between
+// workgroup barriers: a matrix phase (P.V of the group's previous stage, then S^T = K Q^T of
+// its current one: 32 MFMAs per wave at d = 128) and a vector phase (mask, online softmax
+// and exponentials of the current stage, plus transposing the stage's V into ready-made
+// MFMA operands in LDS).  Group 1 runs one phase behind group 0, so in every phase each SIMD
+// holds one wave issuing MFMAs and one issuing vector instructions, and the two execute side
+// by side.  Staging V^T moves the transposing LDS reads out of the matrix phase, whose every
+// operand is then a single 16-byte read (a wave can only keep a few LDS reads in flight, so
+// their count bounds the matrix phase).  Each group keeps its own softmax state over its
+// stages; the two are merged at the end.  K and V stages are double-buffered per group and
+// loaded two to three phases before they are read.
+//
+// The softmax reference max is lazy: it moves only when a stage's max exceeds it by more
+// than 2^8 in exp2 units, so O is rescaled a few times per tile instead of at most stages.
+// Probabilities are then bounded by 2^8 instead of 1, which fp32 sums and bf16 operands hold
+// with the same relative precision; the result is the same softmax.
+template <int D>
+struct PPCfg {
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kChunks = D / 8;               // 16-byte chunks per row
+  static constexpr int kRowsPerInst = 64 / kChunks;   // rows per 64-lane 16-byte load
+  static constexpr int kInst = 16 / kRowsPerInst;     // loads per wave per tensor per stage (one page)
+  static constexpr int kStage = 64 * kRowBytes;       // one 64-key stage of K or V
+  static constexpr int kDS = D / 16;                  // k-steps of QK^T
+  static constexpr int kDB = D / 32;                  // 32-wide d blocks of O^T
+};
+
+constexpr float kLazySlack = 8.f;  // log2 units the reference max may trail the true max
+
+template <int D, bool KPERM>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) fwd_kernel_pp(FwdParams p) {
+  using C = PPCfg<D>;
+  // Stage buffers by slot; group g's stage sits at offset g * kStage of each array.  Four
+  // separate objects, so the compiler can tell reads of one slot from loads into another.
+  __shared__ __attribute__((aligned(1024))) uint8_t sk0[2 * C::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t sk1[2 * C::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t sv0[2 * C::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t sv1[2 * C::kStage];
+  // V^T of each group's current stage as ready-made MFMA operands (operand o: 64 lanes x 16 B)
+  __shared__ __attribute__((aligned(1024))) uint8_t svt[2 * C::kStage];
+  static_assert((C::kDB * 16 + 2) * 64 * 4 <= 2 * C::kStage, "merge buffer fits");
+  static_assert(4 * C::kDB * 1024 == C::kStage, "one 1 KB operand per 16 keys x 32 d");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // stage group
+  const int wr = wave & 3;    // row group, and the page of each stage this wave loads
+  const int hh = lane >> 5;
+
+  const CONST_AS int32_t* pl_ent = (const CONST_AS int32_t*)p.pl_ent;
+  const CONST_AS int32_t* pl_ptr = (const CONST_AS int32_t*)p.pl_ptr;
+  const CONST_AS int32_t* qtiles = (const CONST_AS int32_t*)p.qtiles;
+  const CONST_AS int32_t* kperm = (const CONST_AS int32_t*)p.kperm;
+
+  // ---- work item (XCD-aware: consecutive items share an XCD's L2) ----
+  int work;
+  {
+    const int n = p.n_work, blk = blockIdx.x;
+    const int x = blk & 7, i = blk >> 3, q = n >> 3, r = n & 7;
+    work = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
+  }
+  const int bh = work / p.n_qtiles;
+  const int t = work - bh * p.n_qtiles;
+  const int b = bh / p.Hq;
+  const int h = bh - b * p.Hq;
+  const int g = h / p.grp;
+  const int qt_row0 = qtiles[4 * t], qt_rows = qtiles[4 * t + 1], qt_qblock = qtiles[4 * t + 2];
+  const int unit = (b * p.ub_mul) * p.sel_nh + h / p.uh_div;
+  const int row = unit * p.nqb + qt_qblock;
+  const int e0 = pl_ptr[row];
+  const int e1 = pl_ptr[row + 1];
+  const int ns = (e1 - e0 + 3) >> 2;        // 64-key stages
+  const int my_n = (ns + 1 - grp) >> 1;     // this group's stages: global 2j + grp, j < my_n
+
+  // ---- Q^T operand: lane holds query (lane % 32) of its row group, 8 d per k-step ----
+  const int qrow = wr * 32 + (lane & 31);
+  const bool qvalid = qrow < qt_rows;
+  const int qslot = qt_row0 + (qvalid ? qrow : 0);
+  const int qtok = p.qperm ? p.qperm[qslot] : qslot;
+  bf16x8 qreg[C::kDS];
+  {
+    const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.q_sb + (int64_t)qtok * p.q_sn +
+                       (int64_t)h * p.q_sh + hh * 8;
+#pragma unroll
+    for (int s = 0; s < C::kDS; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
+  }
+  int thr = 0x7ffffffe;  // causal: a key is kept iff its token <= thr
+  if (p.causal) {
+    const int64_t qp = p.q_pos0 + (int64_t)qtok;
+    thr = qp < -1 ? -1 : (qp > 0x7ffffffe ? 0x7ffffffe : (int)qp);
+  }
+  const int64_t minq_pos = p.q_pos0 + qt_row0 + wr * 32;  // smallest query position of the wave (identity Q)
+
+  // ---- loader: page wr of a stage -> rows wr * 16 .. + 15 of the group's stage buffer ----
+  const int ld_lr = lane / C::kChunks;
+  const int ld_pc = lane % C::kChunks;
+  const char* kslice = reinterpret_cast<const char*>(p.k) + ((int64_t)b * p.k_sb + (int64_t)g * p.k_sh) * 2;
+  const char* vslice = reinterpret_cast<const char*>(p.v) + ((int64_t)b * p.v_sb + (int64_t)g * p.v_sh) * 2;
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kslice, (short)0, p.k_extent, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)vslice, (short)0, p.v_extent, 0x00020000);
+  int ld_rip[C::kInst], ld_cb[C::kInst];
+  uint32_t ld_vk[C::kInst], ld_vv[C::kInst];
+#pragma unroll
+  for (int n = 0; n < C::kInst; ++n) {
+    ld_rip[n] = n * C::kRowsPerInst + ld_lr;  // row inside the page
+    ld_cb[n] = (ld_pc ^ swz<D>(ld_rip[n])) * 16;
+    ld_vk[n] = (uint32_t)ld_rip[n] * p.k_sn_bytes + ld_cb[n];
+    ld_vv[n] = (uint32_t)ld_rip[n] * p.v_sn_bytes + ld_cb[n];
+  }
+  const int goff = grp * C::kStage;                      // this group's stage in a slot array
+  const int woff = goff + wr * 16 * C::kRowBytes;        // this wave's page in it
+
+  // The four page entries of local stage j (global 2j + grp), zero past the list (the entry
+  // array is zero-padded past its end, so the scalar load stays in bounds).  They are loaded
+  // two phases ahead of their first use and kept in scalar registers.
+  // The raw words are only checked against the list's end where they are used, so that no
+  // instruction of the loading phase waits for them.
+  auto entries = [&](int j) __attribute__((always_inline)) {
+    return *(const CONST_AS SVec<4>*)(pl_ent + e0 + 4 * (2 * j + grp));
+  };
+  auto valid = [&](const SVec<4>& raw, int j) __attribute__((always_inline)) {
+    const int es = e0 + 4 * (2 * j + grp);
+    SVec<4> r;
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) r[pp] = es + pp < e1 ? raw[pp] : 0;
+    return r;
+  };
+  auto mine = [&](const SVec<4>& raw, int j) __attribute__((always_inline)) {
+    const int e = e0 + 4 * (2 * j + grp) + wr;
+    const int w = wr == 0 ? raw[0] : (wr == 1 ? raw[1] : (wr == 2 ? raw[2] : raw[3]));
+    return e < e1 ? w : 0;
+  };
+
+  // Loads of this wave's page (entry ent) of a stage: per-lane offsets first (prep), then one
+  // 1 KB global->LDS load per call of fire.  Stages past the list have zero entries: every row
+  // then loads token 0 (or slot 0), which nobody reads.  The loads are never skipped, so every
+  // phase leaves the same number in flight.  A CU accepts such loads at a limited rate and a
+  // wave stalls while its load waits, so each phase spreads its loads over its work.
+  struct PageLoad {
+    uint32_t voff[C::kInst];
+    uint32_t soff;
+  };
+  auto prep = [&](int ent, uint32_t sn_bytes, const uint32_t (&vfull)[C::kInst]) __attribute__((always_inline)) {
+    const int nv = ent & 31, slot0 = ent >> 5;
+    PageLoad L;
+    if constexpr (KPERM) {
+      // the page's 16 slot tokens as one scalar load (the permutation is padded by 16)
+      const SVec<16> tk = *(const CONST_AS SVec<16>*)(kperm + slot0);
+#pragma unroll
+      for (int n = 0; n < C::kInst; ++n) {
+        int tok = tk[n * C::kRowsPerInst];
+#pragma unroll
+        for (int r = 1; r < C::kRowsPerInst; ++r) tok = ld_lr == r ? tk[n * C::kRowsPerInst + r] : tok;
+        tok = ld_rip[n] < nv ? tok : tk[0];
+        L.voff[n] = __umul24((uint32_t)tok, sn_bytes) + ld_cb[n];
+      }
+      L.soff = 0;
+    } else {
+#pragma unroll
+      for (int n = 0; n < C::kInst; ++n) L.voff[n] = ld_rip[n] < nv ? vfull[n] : (uint32_t)ld_cb[n];
+      L.soff = (uint32_t)slot0 * sn_bytes;
+    }
+    return L;
+  };
+  auto fire = [&](const PageLoad& L, const __amdgpu_buffer_rsrc_t& rsrc, uint8_t* buf, int n) __attribute__((always_inline)) {
+    if (n < C::kInst)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)(buf + woff + n * C::kRowsPerInst * C::kRowBytes), 16,
+                                               (int)L.voff[n], (int)L.soff, 0, 0);
+  };
+  auto issue = [&](int ent, const __amdgpu_buffer_rsrc_t& rsrc, uint32_t sn_bytes, const uint32_t (&vfull)[C::kInst],
+                   uint8_t* buf) __attribute__((always_inline)) {
+    const PageLoad L = prep(ent, sn_bytes, vfull);
+#pragma unroll
+    for (int n = 0; n < C::kInst; ++n) fire(L, rsrc, buf, n);
+  };
+
+  // ---- per-wave state: softmax of the group's stages, O^T, P of the last stage ----
+  float mref = kNegInf;  // reference max, scaled to exp2 units
+  float l_run = 0.f;
+  f32x16 oacc[C::kDB];
+#pragma unroll
+  for (int db = 0; db < C::kDB; ++db) oacc[db] = f32x16{};
+  f32x16 sacc[2];
+  bf16x8 pbuf[4];
+  const float sl2 = p.scale_log2;
+
+  int nbar = 0;
+  auto bar = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    ++nbar;
+  };
+
+  // Per-lane LDS byte offsets inside the group's stage, so that slot arrays, key blocks and
+  // 16-key chunks all become immediate offsets of a few address registers.  K operand of
+  // k-step s: row lane % 32 (+ 32 per key block), logical chunk 2s + hh.  V^T operand of d
+  // block db: transposed reads of keys 4hh + v_rr and 4hh + v_rr + 8 (+ 16 per chunk).  A
+  // row's swizzle depends only on its low four bits, which the block and chunk steps keep.
+  uint32_t kofs[C::kDS], vofa[C::kDB], vofb[C::kDB];
+  {
+    const int r = lane & 31;
+#pragma unroll
+    for (int s = 0; s < C::kDS; ++s) kofs[s] = goff + r * C::kRowBytes + (((2 * s + hh) ^ swz<D>(r)) * 16);
+    const int v_rr = (lane & 15) >> 2, v_qq = lane & 3, v_dsub = (lane >> 4) & 1;
+    const int key_a = 4 * hh + v_rr, key_b = key_a + 8;
+#pragma unroll
+    for (int db = 0; db < C::kDB; ++db) {
+      const int lc = 4 * db + 2 * v_dsub + (v_qq >> 1);
+      const int off_in = (v_qq & 1) * 8;
+      vofa[db] = goff + key_a * C::kRowBytes + ((lc ^ swz<D>(key_a)) * 16) + off_in;
+      vofb[db] = goff + key_b * C::kRowBytes + ((lc ^ swz<D>(key_b)) * 16) + off_in;
+    }
+  }
+
+  // Transposed V: wave wr turns the 16 keys of chunk wr of the group's V stage at vb into the
+  // V^T operands (chunk wr, d block db) of the next matrix phase, each stored as 64 lanes x
+  // 16 bytes, so that phase reads every operand with one conflict-free 16-byte load.
+  const uint32_t opofs = goff + lane * 16;
+  auto transpose_v = [&](const uint8_t* vb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < C::kDB; ++db) {
+      const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(vb + vofa[db] + wr * 16 * C::kRowBytes));
+      const bf16x4 vq = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(vb + vofb[db] + wr * 16 * C::kRowBytes));
+      *reinterpret_cast<bf16x8*>(svt + opofs + (wr * C::kDB + db) * 1024) =
+          bf16x8{va[0], va[1], va[2], va[3], vq[0], vq[1], vq[2], vq[3]};
+    }
+  };
+
+  // Matrix phase: O^T += V^T P^T over the staged V^T operands (PV), then S^T = K Q^T over the
+  // K stage at kb (QK).  The products run as one list (PV: 16-key chunk c, d block db; QK:
+  // k-step s, key block j) whose operands are read kLead products ahead of their use, so
+  // the matrix core does not stall on LDS latency between products.
+  constexpr int kNPV = 4 * C::kDB, kNQK = 2 * C::kDS, kLead = 4;
+  auto mphase = [&](const uint8_t* kb, auto pv_tag, auto qk_tag, const PageLoad* ldk, uint8_t* kdst, const PageLoad* ldv,
+                    uint8_t* vdst) __attribute__((always_inline)) {
+    constexpr bool PV = decltype(pv_tag)::value, QK = decltype(qk_tag)::value;
+    constexpr int n0 = PV ? 0 : kNPV;
+    constexpr int n1 = QK ? kNPV + kNQK : kNPV;
+    constexpr int kSpread = (n1 - n0) / (2 * C::kInst);  // one load before every kSpread-th product
+    // The SIMD's arbiter favours older waves; raising the matrix wave's priority keeps its
+    // MFMAs flowing whichever group is in the vector phase.
+    __builtin_amdgcn_s_setprio(2);
+    bf16x8 ring[kLead + 1];
+    auto load = [&](auto it) __attribute__((always_inline)) {
+      constexpr int i = decltype(it)::value;
+      if constexpr (i < kNPV) {
+        ring[(i - n0) % (kLead + 1)] = *reinterpret_cast<const bf16x8*>(svt + opofs + i * 1024);
+      } else {
+        constexpr int s = (i - kNPV) / 2, j = (i - kNPV) % 2;
+        ring[(i - n0) % (kLead + 1)] = *reinterpret_cast<const bf16x8*>(kb + kofs[s] + j * 32 * C::kRowBytes);
+      }
+    };
+    auto mma = [&](auto it) __attribute__((always_inline)) {
+      constexpr int i = decltype(it)::value;
+      const bf16x8 a = ring[(i - n0) % (kLead + 1)];
+      if constexpr (i < kNPV) {
+        constexpr int c = i / C::kDB, db = i % C::kDB;
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pbuf[c], oacc[db], 0, 0, 0);
+      } else {
+        constexpr int s = (i - kNPV) / 2, j = (i - kNPV) % 2;
+        sacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], s == 0 ? f32x16{} : sacc[j], 0, 0, 0);
+      }
+    };
+    static_for<n0, (n0 + kLead < n1 ? n0 + kLead : n1)>(load);
+    static_for<n0, n1>([&](auto it) __attribute__((always_inline)) {
+      constexpr int i = decltype(it)::value;
+      if constexpr ((i - n0) % kSpread == 0) {
+        constexpr int t = (i - n0) / kSpread;
+        if constexpr (t < C::kInst) {
+          if (ldk) fire(*ldk, krsrc, kdst, t);
+        } else if constexpr (t < 2 * C::kInst) {
+          if (ldv) fire(*ldv, vrsrc, vdst, t - C::kInst);
+        }
+      }
+      if constexpr (i + kLead < n1) load(IntTag<i + kLead>{});
+      mma(it);
+    });
+    // keep the order: operand reads kLead products ahead of the MFMAs, loads spread out
+    __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
+    static_for<n0, n1>([&](auto it) __attribute__((always_inline)) {
+      constexpr int i = decltype(it)::value;
+      if constexpr ((i - n0) % kSpread == 0 && (i - n0) / kSpread < 2 * C::kInst) {
+        if (ldk) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+      if constexpr (i + kLead < n1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    });
+    // the products stay in this phase (see pin_vector_phase)
+    pin(sacc[0]);
+    pin(sacc[1]);
+#pragma unroll
+    for (int db = 0; db < C::kDB; ++db) pin(oacc[db]);
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // Phases only overlap if each one's instructions stay in it.  The compiler would otherwise
+  // sink the exponentials and conversions of a vector phase down to their use by the next
+  // matrix phase's MFMAs (and could hoist matrix work the other way), so the results of each
+  // phase are tied to its end by empty asm statements that use them.
+  auto pin_vector_phase = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) pin(pbuf[c]);
+    pin(l_run);
+    pin(mref);
+#pragma unroll
+    for (int db = 0; db < C::kDB; ++db) pin(oacc[db]);
+  };
+
+  // Mask, online softmax and P of a stage with page entries ev (S^T in sacc).
+  auto softmax = [&](const SVec<4>& ev, auto&& at) __attribute__((always_inline)) {
+    int ment[4];
+    bool need = false;
+    int maxkey = -1;
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      ment[pp] = ev[pp];
+      const int nv = ment[pp] & 31;
+      need |= nv < 16;
+      const int last = (ment[pp] >> 5) + nv - 1;
+      maxkey = (nv > 0 && last > maxkey) ? last : maxkey;
+    }
+    if (p.causal) need |= p.qperm ? true : ((int64_t)maxkey > minq_pos);
+    if (need) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // key 32kb + 8i + 4hh + jj is row 8(i&1) + 4hh + jj of page 2kb + i/2
+          const int ent = ment[2 * kb + (i >> 1)];
+          int lim = (ent & 31) - 1;
+          if (p.causal) lim = min(lim, thr - (ent >> 5));
+          const int rip0 = 8 * (i & 1) + 4 * hh;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            if (rip0 + jj > lim) sacc[kb][4 * i + jj] = kNegInf;
+        }
+      }
+    }
+    float mt = fmaxf(max16(sacc[0]), max16(sacc[1]));
+    mt = xor32_max(mt) * sl2;
+    const bool grow = mt > mref + kLazySlack;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float alpha = grow ? __builtin_amdgcn_exp2f(mref - mt) : 1.f;
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db) oacc[db] *= alpha;
+      l_run *= alpha;
+      mref = grow ? mt : mref;
+    }
+    const float nb = mref == kNegInf ? 0.f : -mref;
+    at(0);
+    float ps[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (kb == 1) at(1);
+      float pe[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][e], sl2, nb));
+        pbuf[2 * kb + (e >> 3)][e & 7] = (__bf16)pe[e];
+      }
+      ps[kb] = sum16(pe);
+    }
+    l_run += ps[0] + ps[1];
+    pin_vector_phase();
+  };
+
+  // Load schedule of local stage j: matrix phase j issues K(j + 1) and V(j + 1), spread over
+  // its products (K(j + 1)'s slot held K(j - 1), read in matrix phase j - 1; V(j + 1)'s held
+  // V(j - 1), transposed in vector phase j - 1).  Matrix phase j ends by waiting for V(j),
+  // vector phase j for K(j + 1).  Vector phases issue no loads: their waves are the busier
+  // ones, and a wave stalls while a load waits for the CU's memory pipeline.  Page entries of
+  // stage j + 3 are loaded in vector phase j, after its LDS work, so that no LDS wait ever
+  // covers a scalar load in flight.
+  if (ns > 0) {
+    SVec<4> x0 = entries(0), x1 = entries(1), x2 = entries(2);  // raw entries of stages j, j + 1, j + 2
+    issue(mine(x0, 0), krsrc, p.k_sn_bytes, ld_vk, sk0);
+    issue(mine(x0, 0), vrsrc, p.v_sn_bytes, ld_vv, sv0);
+    wait_vmcnt<C::kInst>();  // K of stage 0 landed
+    bar();
+    if (grp == 1) bar();  // group 1 runs one phase behind
+    if (my_n > 0) {
+      // matrix phase: P.V of the previous stage (if PV), S of the stage in kbuf (if QK), loads
+      // of stage jn (entry word ent) into kdst / vdst
+      auto mph = [&](auto pv_tag, auto qk_tag, const uint8_t* kbuf, int ent, uint8_t* kdst, uint8_t* vdst)
+                     __attribute__((always_inline)) {
+        const PageLoad lk = prep(ent, p.k_sn_bytes, ld_vk);
+        const PageLoad lv = prep(ent, p.v_sn_bytes, ld_vv);
+        mphase(kbuf, pv_tag, qk_tag, &lk, kdst, &lv, vdst);
+        wait_vmcnt<2 * C::kInst>();  // V of the phase's own stage landed
+        bar();
+      };
+      // vector phase of stage j: V(j) transposed from vbuf, entries of stage j + 3 loaded,
+      // softmax with entries ej
+      auto vph = [&](int j, const SVec<4>& ej, const uint8_t* vbuf) __attribute__((always_inline)) {
+        transpose_v(vbuf);
+        __builtin_amdgcn_sched_barrier(0);
+        const SVec<4> next = entries(j + 3);
+        softmax(ej, [](int) {});
+        wait_vmcnt<C::kInst>();  // K of the next stage landed
+        bar();
+        return next;
+      };
+      mph(BoolTag<false>{}, BoolTag<true>{}, sk0, mine(x1, 1), sk1, sv1);
+      const SVec<4> x3 = vph(0, valid(x0, 0), sv0);
+      x0 = x1;
+      x1 = x2;
+      x2 = x3;
+      int j = 1;
+      for (; j + 1 < my_n; j += 2) {
+        mph(BoolTag<true>{}, BoolTag<true>{}, sk1, mine(x1, j + 1), sk0, sv0);  // P.V of j - 1, S of j (odd)
+        const SVec<4> x3n = vph(j, valid(x0, j), sv1);
+        mph(BoolTag<true>{}, BoolTag<true>{}, sk0, mine(x2, j + 2), sk1, sv1);  // P.V of j, S of j + 1 (even)
+        const SVec<4> x4 = vph(j + 1, valid(x1, j + 1), sv0);
+        x0 = x2;
+        x1 = x3n;
+        x2 = x4;
+      }
+      if (j < my_n) {
+        mph(BoolTag<true>{}, BoolTag<true>{}, sk1, mine(x1, j + 1), sk0, sv0);
+        vph(j, valid(x0, j), sv1);
+      }
+      mphase(sk0, BoolTag<true>{}, BoolTag<false>{}, nullptr, nullptr, nullptr, nullptr);  // P.V of the last stage
+      bar();
+    }
+    // both groups pass the same number of barriers
+    const int n0 = (ns + 1) >> 1, n1 = ns >> 1;
+    const int c0 = 2 * n0 + 2, c1 = n1 > 0 ? 2 * n1 + 3 : 2;
+    const int total = c0 > c1 ? c0 : c1;
+    while (nbar < total) bar();
+    wait_vmcnt<0>();  // loads past the list may still be landing in the stage buffers
+  }
+
+  // ---- finish: combine lane halves, merge the two groups, write O and LSE ----
+  float l_tot = xor32_sum(l_run);
+  __syncthreads();
+  float* mb = reinterpret_cast<float*>(wr == 0 ? sk0 : (wr == 1 ? sk1 : (wr == 2 ? sv0 : sv1)));
+  if (grp == 1) {
+#pragma unroll
+    for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mb[(db * 16 + e) * 64 + lane] = oacc[db][e];
+    mb[(C::kDB * 16) * 64 + lane] = mref;
+    mb[(C::kDB * 16 + 1) * 64 + lane] = l_tot;
+  }
+  __syncthreads();
+  if (grp == 1) return;
+  const float m1 = mb[(C::kDB * 16) * 64 + lane];
+  const float l1 = mb[(C::kDB * 16 + 1) * 64 + lane];
+  const float mm = fmaxf(mref, m1);
+  const float mu = (mm == kNegInf) ? 0.f : mm;
+  const float a0 = __builtin_amdgcn_exp2f(mref - mu);
+  const float a1 = __builtin_amdgcn_exp2f(m1 - mu);
+#pragma unroll
+  for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[db][e] = oacc[db][e] * a0 + mb[(db * 16 + e) * 64 + lane] * a1;
+  l_tot = l_tot * a0 + l1 * a1;
+
+  if (!qvalid) return;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  __bf16* op = reinterpret_cast<__bf16*>(p.o) + (int64_t)b * p.o_sb + (int64_t)qtok * p.o_sn + (int64_t)h * p.o_sh;
+#pragma unroll
+  for (int db = 0; db < C::kDB; ++db) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bf16x4 v4;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) v4[jj] = (__bf16)(oacc[db][4 * i + jj] * inv);
+      *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * i + 4 * hh) = v4;
+    }
+  }
+  if (hh == 0) {
+    const float lse = l_tot > 0.f ? mm * kLn2 + __logf(l_tot) : kNegInf;
+    p.lse[((int64_t)b * p.Hq + h) * p.Nq + qtok] = lse;
+  }
+}
+
 template <int D, int NRG, int NKG, int KB>
 static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
   if (p.n_work <= 0) return hipSuccess;
@@ -485,10 +1000,30 @@ static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
 #define BSATTN_KB64 2
 #endif
 
+template <int D>
+static hipError_t launch_pp(const FwdParams& p, hipStream_t stream) {
+  if (p.n_work <= 0) return hipSuccess;
+  if (p.kperm)
+    hipLaunchKernelGGL((fwd_kernel_pp<D, true>), dim3(p.n_work), dim3(512), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fwd_kernel_pp<D, false>), dim3(p.n_work), dim3(512), 0, stream, p);
+  return hipGetLastError();
+}
+
+// The ping-pong kernel runs 128x128 tiles unless keys are permuted under a causal mask (its
+// mask reads no key tokens) or the permuted offsets would not fit 24-bit products.
+static bool pp_supported(const FwdParams& p) {
+  if (!p.kperm) return true;
+  return !p.causal && p.Nk < (1 << 24) && p.k_sn_bytes < (1u << 24) && p.v_sn_bytes < (1u << 24);
+}
+
 hipError_t launch_fwd_shape(const FwdParams& p, int shape, int d, hipStream_t stream) {
-  if (d == 128)
-    return shape == 0 ? launch_one<128, 4, 1, BSATTN_KB128>(p, stream) : launch_one<128, 2, 2, BSATTN_KB64>(p, stream);
-  return shape == 0 ? launch_one<64, 4, 1, BSATTN_KB128>(p, stream) : launch_one<64, 2, 2, BSATTN_KB64>(p, stream);
+  if (d == 128) {
+    if (shape == 0) return pp_supported(p) ? launch_pp<128>(p, stream) : launch_one<128, 4, 1, BSATTN_KB128>(p, stream);
+    return launch_one<128, 2, 2, BSATTN_KB64>(p, stream);
+  }
+  if (shape == 0) return pp_supported(p) ? launch_pp<64>(p, stream) : launch_one<64, 4, 1, BSATTN_KB128>(p, stream);
+  return launch_one<64, 2, 2, BSATTN_KB64>(p, stream);
 }
 
 }  // namespace bsattn

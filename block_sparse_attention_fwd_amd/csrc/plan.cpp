@@ -215,7 +215,8 @@ int build_plan(const bsattn_problem& prob, const bsattn_layout& ql, const bsattn
   p->off_qperm = off;
   if (p->has_qperm) off = align256(off + sizeof(int32_t) * size_t(Nq));
   p->off_kperm = off;
-  if (p->has_kperm) off = align256(off + sizeof(int32_t) * size_t(Nk));
+  // zero padding past the key permutation: a kernel reads a page's 16 slots at once
+  if (p->has_kperm) off = align256(off + sizeof(int32_t) * (size_t(Nk) + kPermPad));
   p->image.assign(std::max<size_t>(off, 256), 0);
 
   uint8_t* img = p->image.data();

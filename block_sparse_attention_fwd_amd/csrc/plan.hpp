@@ -23,8 +23,9 @@ constexpr int kPagesPerKTile[kShapes] = {8, 16};
 // page-list entries are packed as (first slot << 5) | valid rows
 constexpr int kEntryShift = 5;
 constexpr int64_t kMaxSlots = int64_t(1) << (31 - kEntryShift);
-// zero entries after the page lists (kernels read up to 16 entries past a list's end)
-constexpr size_t kEntryPad = 32;
+// zero entries after the page lists (kernels read up to 27 entries past a list's end)
+constexpr size_t kEntryPad = 64;
+constexpr size_t kPermPad = 16;
 
 }  // namespace bsattn
 
