@@ -687,8 +687,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   f32x16 oacc[C::kDB];
 #pragma unroll
   for (int db = 0; db < C::kDB; ++db) oacc[db] = f32x16{};
-  f32x16 sacc[2];
-  bf16x8 pbuf[4];
+  f32x16 sacc[2];  // S^T of the stage; after the vector phase, its P (fp32) until the next P.V
   const float sl2 = p.scale_log2;
 
   int nbar = 0;
@@ -724,14 +723,22 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   // V^T operands (chunk wr, d block db) of the next matrix phase, each stored as 64 lanes x
   // 16 bytes, so that phase reads every operand with one conflict-free 16-byte load.
   const uint32_t opofs = goff + lane * 16;
-  auto transpose_v = [&](const uint8_t* vb) __attribute__((always_inline)) {
+  struct VtOps {
+    bf16x8 op[C::kDB];
+  };
+  auto transpose_read = [&](const uint8_t* vb) __attribute__((always_inline)) {
+    VtOps t;
 #pragma unroll
     for (int db = 0; db < C::kDB; ++db) {
       const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(vb + vofa[db] + wr * 16 * C::kRowBytes));
       const bf16x4 vq = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(vb + vofb[db] + wr * 16 * C::kRowBytes));
-      *reinterpret_cast<bf16x8*>(svt + opofs + (wr * C::kDB + db) * 1024) =
-          bf16x8{va[0], va[1], va[2], va[3], vq[0], vq[1], vq[2], vq[3]};
+      t.op[db] = bf16x8{va[0], va[1], va[2], va[3], vq[0], vq[1], vq[2], vq[3]};
     }
+    return t;
+  };
+  auto transpose_write = [&](const VtOps& t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < C::kDB; ++db) *reinterpret_cast<bf16x8*>(svt + opofs + (wr * C::kDB + db) * 1024) = t.op[db];
   };
 
   // Matrix phase: O^T += V^T P^T over the staged V^T operands (PV), then S^T = K Q^T over the
@@ -748,6 +755,19 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     // The SIMD's arbiter favours older waves; raising the matrix wave's priority keeps its
     // MFMAs flowing whichever group is in the vector phase.
     __builtin_amdgcn_s_setprio(2);
+    // P of the previous stage (fp32 in sacc) as bf16 operands, and its row sum: vector work
+    // that this wave's idle VALU slots absorb while its MFMAs run
+    bf16x8 pbuf[4];
+    if constexpr (PV) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) pbuf[2 * kb + (e >> 3)][e & 7] = (__bf16)sacc[kb][e];
+      float pr[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) pr[e] = sacc[0][e] + sacc[1][e];
+      l_run += sum16(pr);
+    }
     bf16x8 ring[kLead + 1];
     auto load = [&](auto it) __attribute__((always_inline)) {
       constexpr int i = decltype(it)::value;
@@ -796,6 +816,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     // the products stay in this phase (see pin_vector_phase)
     pin(sacc[0]);
     pin(sacc[1]);
+    pin(l_run);
 #pragma unroll
     for (int db = 0; db < C::kDB; ++db) pin(oacc[db]);
     __builtin_amdgcn_s_setprio(0);
@@ -806,15 +827,16 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   // matrix phase's MFMAs (and could hoist matrix work the other way), so the results of each
   // phase are tied to its end by empty asm statements that use them.
   auto pin_vector_phase = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) pin(pbuf[c]);
+    pin(sacc[0]);
+    pin(sacc[1]);
     pin(l_run);
     pin(mref);
 #pragma unroll
     for (int db = 0; db < C::kDB; ++db) pin(oacc[db]);
   };
 
-  // Mask, online softmax and P of a stage with page entries ev (S^T in sacc).
+  // Mask, online softmax and P (in place, fp32) of a stage with page entries ev (S^T in sacc);
+  // its row sum and bf16 conversion happen in the next matrix phase.
   auto softmax = [&](const SVec<4>& ev, auto&& at) __attribute__((always_inline)) {
     int ment[4];
     bool need = false;
@@ -856,19 +878,20 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     const float nb = mref == kNegInf ? 0.f : -mref;
     at(0);
-    float ps[2];
+    // all scalings, then all exponentials, each in place: 32 independent operations per step
+    // instead of 32 dependent pairs through one temporary register
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[kb][e] = __builtin_fmaf(sacc[kb][e], sl2, nb);
+    pin(sacc[0]);
+    pin(sacc[1]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       if (kb == 1) at(1);
-      float pe[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][e], sl2, nb));
-        pbuf[2 * kb + (e >> 3)][e & 7] = (__bf16)pe[e];
-      }
-      ps[kb] = sum16(pe);
+      for (int e = 0; e < 16; ++e) sacc[kb][e] = __builtin_amdgcn_exp2f(sacc[kb][e]);
     }
-    l_run += ps[0] + ps[1];
     pin_vector_phase();
   };
 
@@ -900,7 +923,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       // vector phase of stage j: V(j) transposed from vbuf, entries of stage j + 3 loaded,
       // softmax with entries ej
       auto vph = [&](int j, const SVec<4>& ej, const uint8_t* vbuf) __attribute__((always_inline)) {
-        transpose_v(vbuf);
+        transpose_write(transpose_read(vbuf));
         __builtin_amdgcn_sched_barrier(0);
         const SVec<4> next = entries(j + 3);
         softmax(ej, [](int) {});
