@@ -163,7 +163,7 @@ def main():
     achieved = 4.0 * w.d * u128 / (k128 * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(args.workload, "128x128"),
-                "kernel": f"fwd_kernel<{w.d},4,1> (128x128 tiles)", "kernel_ms": round(k128, 4),
+                "kernel": f"fwd_kernel_pp<{w.d}> (128x128 tiles)", "kernel_ms": round(k128, 4),
                 "useful_pairs_per_launch": u128}
 
     cpu = None
