@@ -41,6 +41,11 @@ using SVec = int __attribute__((ext_vector_type(N), aligned(4)));
 #define CONST_AS __attribute__((address_space(4)))
 
 constexpr float kNegInf = -__builtin_huge_valf();
+
+// Page-list entry word: valid rows in bits 0..4, first slot in bits 5..30, and bit 31 set on
+// the entries of a 4-entry stage that holds a partial page or ends past its list.
+__device__ __forceinline__ int ent_nv(int ent) { return ent & 31; }
+__device__ __forceinline__ int ent_slot(int ent) { return (ent >> 5) & ((1 << 26) - 1); }
 constexpr float kLn2 = 0.693147180559945309f;
 
 // Ties a register value to this point of the program: an empty asm statement that uses it.
@@ -267,7 +272,7 @@ __global__ void __launch_bounds__(256)
       for (int n = 0; n < C::kInst; ++n) {
         const int ent = ents[(n * C::kRowsPerInst) >> 4];
         const int nv = ent & 31, rip = ld_rip[n % kPeriod];
-        const int tok = p.kperm[(ent >> 5) + (rip < nv ? rip : 0)];
+        const int tok = p.kperm[ent_slot(ent) + (rip < nv ? rip : 0)];
         ldtok[n] = tok;
         if (ld_pc == 0) ktok_lds[wave * C::kRowsPerWave + n * C::kRowsPerInst + ld_lr] = rip < nv ? tok : 0x7fffffff;
       }
@@ -279,7 +284,7 @@ __global__ void __launch_bounds__(256)
       ment[pp] = es + pp < e1 ? sv[pp] : 0;
       const int nv = ment[pp] & 31;
       need |= nv < 16;
-      const int last = (ment[pp] >> 5) + nv - 1;
+      const int last = ent_slot(ment[pp]) + nv - 1;
       maxkey = (nv > 0 && last > maxkey) ? last : maxkey;
     }
     if (p.causal) {
@@ -306,7 +311,7 @@ __global__ void __launch_bounds__(256)
         const int ent = ents[(n * C::kRowsPerInst) >> 4];
         voff[n] = vfull[n % kPeriod];
         if (!ents_full && ld_rip[n % kPeriod] >= (ent & 31)) voff[n] = (uint32_t)ld_cb[n % kPeriod];
-        soff[n] = (uint32_t)(ent >> 5) * sn_bytes;
+        soff[n] = (uint32_t)ent_slot(ent) * sn_bytes;
       }
     }
 #pragma unroll
@@ -376,7 +381,7 @@ __global__ void __launch_bounds__(256)
             // key 32kb + 8i + 4hh + j is row 8(i&1) + 4hh + j of page 2kb + i/2
             const int ent = ment[2 * kb + (i >> 1)];
             int lim = (ent & 31) - 1;
-            if (p.causal) lim = min(lim, thr - (ent >> 5));
+            if (p.causal) lim = min(lim, thr - ent_slot(ent));
             const int rip0 = 8 * (i & 1) + 4 * hh;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
@@ -648,7 +653,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     uint32_t soff;
   };
   auto prep = [&](int ent, uint32_t sn_bytes, const uint32_t (&vfull)[C::kInst]) __attribute__((always_inline)) {
-    const int nv = ent & 31, slot0 = ent >> 5;
+    const int nv = ent_nv(ent), slot0 = ent_slot(ent);
     PageLoad L;
     if constexpr (KPERM) {
       // the page's 16 slot tokens as one scalar load (the permutation is padded by 16)
@@ -837,20 +842,26 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   // Mask, online softmax and P (in place, fp32) of a stage with page entries ev (S^T in sacc);
   // its row sum and bf16 conversion happen in the next matrix phase.
-  auto softmax = [&](const SVec<4>& ev, auto&& at) __attribute__((always_inline)) {
-    int ment[4];
-    bool need = false;
-    int maxkey = -1;
+  auto softmax = [&](const SVec<4>& raw, int j, auto&& at) __attribute__((always_inline)) {
+    // the planner flags stages with a partial page or a cut-short end (bit 31 of the first
+    // entry); causal problems also mask stages whose keys may follow a query
+    bool need = raw[0] < 0;
+    if (p.causal) {
+      const SVec<4> ev = valid(raw, j);
+      int maxkey = -1;
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      ment[pp] = ev[pp];
-      const int nv = ment[pp] & 31;
-      need |= nv < 16;
-      const int last = (ment[pp] >> 5) + nv - 1;
-      maxkey = (nv > 0 && last > maxkey) ? last : maxkey;
+      for (int pp = 0; pp < 4; ++pp) {
+        const int nv = ent_nv(ev[pp]);
+        const int last = ent_slot(ev[pp]) + nv - 1;
+        maxkey = (nv > 0 && last > maxkey) ? last : maxkey;
+      }
+      need |= p.qperm ? true : ((int64_t)maxkey > minq_pos);
     }
-    if (p.causal) need |= p.qperm ? true : ((int64_t)maxkey > minq_pos);
     if (need) {
+      const SVec<4> ev = valid(raw, j);
+      int ment[4];
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) ment[pp] = ev[pp];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -858,7 +869,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
           // key 32kb + 8i + 4hh + jj is row 8(i&1) + 4hh + jj of page 2kb + i/2
           const int ent = ment[2 * kb + (i >> 1)];
           int lim = (ent & 31) - 1;
-          if (p.causal) lim = min(lim, thr - (ent >> 5));
+          if (p.causal) lim = min(lim, thr - ent_slot(ent));
           const int rip0 = 8 * (i & 1) + 4 * hh;
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj)
@@ -921,34 +932,34 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
         bar();
       };
       // vector phase of stage j: V(j) transposed from vbuf, entries of stage j + 3 loaded,
-      // softmax with entries ej
+      // softmax with raw entries ej
       auto vph = [&](int j, const SVec<4>& ej, const uint8_t* vbuf) __attribute__((always_inline)) {
         transpose_write(transpose_read(vbuf));
         __builtin_amdgcn_sched_barrier(0);
         const SVec<4> next = entries(j + 3);
-        softmax(ej, [](int) {});
+        softmax(ej, j, [](int) {});
         wait_vmcnt<C::kInst>();  // K of the next stage landed
         bar();
         return next;
       };
       mph(BoolTag<false>{}, BoolTag<true>{}, sk0, mine(x1, 1), sk1, sv1);
-      const SVec<4> x3 = vph(0, valid(x0, 0), sv0);
+      const SVec<4> x3 = vph(0, x0, sv0);
       x0 = x1;
       x1 = x2;
       x2 = x3;
       int j = 1;
       for (; j + 1 < my_n; j += 2) {
         mph(BoolTag<true>{}, BoolTag<true>{}, sk1, mine(x1, j + 1), sk0, sv0);  // P.V of j - 1, S of j (odd)
-        const SVec<4> x3n = vph(j, valid(x0, j), sv1);
+        const SVec<4> x3n = vph(j, x0, sv1);
         mph(BoolTag<true>{}, BoolTag<true>{}, sk0, mine(x2, j + 2), sk1, sv1);  // P.V of j, S of j + 1 (even)
-        const SVec<4> x4 = vph(j + 1, valid(x1, j + 1), sv0);
+        const SVec<4> x4 = vph(j + 1, x1, sv0);
         x0 = x2;
         x1 = x3n;
         x2 = x4;
       }
       if (j < my_n) {
         mph(BoolTag<true>{}, BoolTag<true>{}, sk1, mine(x1, j + 1), sk0, sv0);
-        vph(j, valid(x0, j), sv1);
+        vph(j, x0, sv1);
       }
       mphase(sk0, BoolTag<true>{}, BoolTag<false>{}, nullptr, nullptr, nullptr, nullptr);  // P.V of the last stage
       bar();

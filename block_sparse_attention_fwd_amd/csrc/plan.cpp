@@ -235,6 +235,18 @@ int build_plan(const bsattn_problem& prob, const bsattn_layout& ql, const bsattn
     const int32_t pg = p->pl_pages[e];
     ent[e] = (p->page_slot0[pg] << kEntryShift) | p->page_nvalid[pg];
   }
+  // mask flag: every entry of a kStagePages-entry stage (counted from its list's start) with
+  // a partial page, or cut short by the list's end, carries kEntryMaskBit
+  for (size_t r = 0; r < size_t(n_rows); ++r) {
+    const int64_t a = p->pl_ptr[r], b = p->pl_ptr[r + 1];
+    for (int64_t s0 = a; s0 < b; s0 += kStagePages) {
+      const int64_t s1 = std::min<int64_t>(s0 + kStagePages, b);
+      bool partial = s1 - s0 < kStagePages;
+      for (int64_t e = s0; e < s1; ++e) partial |= (ent[e] & ((1 << kEntryShift) - 1)) < kPage;
+      if (partial)
+        for (int64_t e = s0; e < s1; ++e) ent[e] = int32_t(uint32_t(ent[e]) | kEntryMaskBit);
+    }
+  }
   if (p->has_qperm) std::memcpy(img + p->off_qperm, ql.perm, sizeof(int32_t) * size_t(Nq));
   if (p->has_kperm) std::memcpy(img + p->off_kperm, kl.perm, sizeof(int32_t) * size_t(Nk));
   return BSATTN_OK;

@@ -20,9 +20,13 @@ constexpr int kShapes = 2;
 constexpr int kTileRows[kShapes] = {128, 64};
 constexpr int kTileCols[kShapes] = {128, 256};
 constexpr int kPagesPerKTile[kShapes] = {8, 16};
-// page-list entries are packed as (first slot << 5) | valid rows
+// page-list entries are packed as (first slot << 5) | valid rows, plus kEntryMaskBit on the
+// entries of every 4-entry stage (counted from the start of its list) that holds a partial
+// page or ends past the list: stages without it need no mask for empty page rows
 constexpr int kEntryShift = 5;
-constexpr int64_t kMaxSlots = int64_t(1) << (31 - kEntryShift);
+constexpr int64_t kMaxSlots = int64_t(1) << (31 - kEntryShift);  // slots use bits 5..30
+constexpr uint32_t kEntryMaskBit = 0x80000000u;
+constexpr int kStagePages = 4;
 // zero entries after the page lists (kernels read up to 27 entries past a list's end)
 constexpr size_t kEntryPad = 64;
 constexpr size_t kPermPad = 16;
