@@ -768,10 +768,16 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) pbuf[2 * kb + (e >> 3)][e & 7] = (__bf16)sacc[kb][e];
-      float pr[16];
+      // row sum of the bf16 probabilities (the ones P.V uses): two at a time with v_dot2
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 16; ++e) pr[e] = sacc[0][e] + sacc[1][e];
-      l_run += sum16(pr);
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2)
+          ls[c] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pbuf[c][e], pbuf[c][e + 1]}, one2, ls[c], false);
+      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     }
     bf16x8 ring[kLead + 1];
     auto load = [&](auto it) __attribute__((always_inline)) {
