@@ -155,8 +155,11 @@ int bsattn_plan_export(const bsattn_plan* plan, bsattn_plan_view* view);
  * rows); lse: device float32 [B, Hq, Nq]; scale: the softmax scale, finite and > 0.  Every
  * O row and LSE entry is written.  No allocation, no synchronisation.  Strides must be
  * non-negative, and the K (and V) rows of one (batch, KV head) must lie within 4 GiB of
- * that slice's first element (BSATTN_E_UNSUPPORTED otherwise).  Returns BSATTN_E_STATE when the plan was never
- * uploaded, BSATTN_E_ARG on a null or misaligned pointer, BSATTN_E_HIP on a launch error. */
+ * that slice's first element (BSATTN_E_UNSUPPORTED otherwise).  K and V must be finite in
+ * every row of the key layout, selected or not: page rows past a block's end and empty page
+ * slots load some row of the slice and get probability exactly 0, and 0 times an infinite
+ * V entry would be NaN.  Returns BSATTN_E_STATE when the plan was never uploaded,
+ * BSATTN_E_ARG on a null or misaligned pointer, BSATTN_E_HIP on a launch error. */
 int bsattn_fwd(const bsattn_plan* plan, const void* q, const void* k, const void* v, void* o,
                float* lse, float scale, void* stream);
 
