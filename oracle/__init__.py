@@ -8,7 +8,8 @@ loudly when its HIP library is missing.
 Contents
   attention.py  masked dense softmax attention in float64 (numpy): the full masked
                 score matrix, -inf outside the sparse graph, softmax, times V; plus a
-                pure-Python scalar brute force for tiny inputs.
+                pure-Python scalar brute force for tiny inputs; and the gradients of
+                that function (dQ, dK, dV) for an upstream gradient of O.
   planner.py    the page / tile plan: 16-row K/V pages owned by one block, Q-block
                 routing between 128x128 and 64x256 tiles, per-(unit, Q block) page
                 lists and the useful / physical query-key pair counts.
@@ -28,6 +29,6 @@ Parity status: every function here is pinned by tests that do not re-use its cod
 """
 from .attention import (  # noqa: F401
     bf16_to_f64, token_block_map, selection_unit, selected_blocks, token_mask,
-    masked_attention, brute_force_attention, useful_pairs,
+    masked_attention, brute_force_attention, useful_pairs, masked_attention_bwd, masked_attention_bwd_w,
 )
 from .planner import Plan, build_plan  # noqa: F401

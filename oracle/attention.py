@@ -240,3 +240,139 @@ def brute_force_attention(q, k, v, q_offsets, q_perm, k_offsets, k_perm, sel_nb,
                     O[b][i][h][e] = math.fsum(w[t] * vf[b, keys[t], g, e] for t in range(len(keys))) / tot
                 L[b][h][i] = m + math.log(tot)
     return np.array(O), np.array(L)
+
+
+# ----------------------------------------------------------------------------
+# backward: gradients of the same masked softmax attention
+# ----------------------------------------------------------------------------
+# KPage abstract, sentence 4: masking and K/V-owned pages keep the original sparse graph in
+# the backward pass as well, so the gradients are those of the function above.  With
+# P^_ij = exp(S_ij - LSE_i) (zero outside the graph and on rows without keys) and an
+# upstream gradient dO of O, the chain rule through O = P^ V and the row softmax gives
+#     D_i   = sum_e dO_ie O_ie
+#     dV_j  = sum over query heads of the KV group, sum_i P^_ij dO_i
+#     dS_ij = P^_ij (dO_i . V_j - D_i)
+#     dQ_i  = scale sum_j dS_ij K_j
+#     dK_j  = scale sum over query heads of the group, sum_i dS_ij Q_i
+# D uses the exact O of the forward oracle.
+
+def _widen(x):
+    x = np.asarray(x)
+    return bf16_to_f64(x) if x.dtype == np.uint16 else x.astype(np.float64)
+
+
+def _bwd_head_chunk(qf, kf, vf, dof, t, bq, bk, row_ptr, kblk, unit, nqb, nkb, scale, causal, q_pos0):
+    """Rows t of one (batch, query head): the masked probabilities P^ [len(t), Nk] and
+    dS [len(t), Nk] over the full key width."""
+    s = scale * (qf[t] @ kf.T)
+    msk = token_mask(bq, bk, row_ptr, kblk, unit, nqb, nkb, t, causal, q_pos0)
+    s[~msk] = -np.inf
+    mx = s.max(axis=1)
+    live = mx > -np.inf
+    p = np.zeros_like(s)
+    p[live] = np.exp(s[live] - mx[live, None])
+    l = p.sum(axis=1)
+    p[live] /= l[live, None]
+    o = p @ vf
+    D = np.sum(dof[t] * o, axis=1)
+    dP = dof[t] @ vf.T
+    dS = p * (dP - D[:, None])
+    return p, dS
+
+
+def masked_attention_bwd(q, k, v, do, q_offsets, q_perm, k_offsets, k_perm, sel_nb, sel_nh, sel_row_ptr,
+                         sel_kblk, scale: float, causal: bool = False, q_pos0: int = 0,
+                         q_rows: Optional[Sequence[Tuple[int, int, np.ndarray]]] = None,
+                         k_rows: Optional[Sequence[Tuple[int, int, np.ndarray]]] = None):
+    """Gradients (dQ, dK, dV) of masked softmax attention in float64 for the upstream
+    gradient ``do`` of O (same shape as Q).
+
+    With neither ``q_rows`` nor ``k_rows`` returns full arrays dQ [B, Nq, Hq, d] and
+    dK, dV [B, Nk, Hkv, d].  With ``q_rows`` = [(b, h, query tokens), ...] and/or
+    ``k_rows`` = [(b, g, key tokens), ...] returns (list of dQ rows, list of (dK rows,
+    dV rows)); a key's rows sum over every query head of KV group g and over every query
+    in the graph with it, whose full rows are computed for their softmax statistics.
+    """
+    B, Nq, Hq, d = np.asarray(q).shape
+    Nk, Hkv = np.asarray(k).shape[1], np.asarray(k).shape[2]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    grp = Hq // Hkv
+    bq = token_block_map(q_offsets, q_perm, Nq)
+    bk = token_block_map(k_offsets, k_perm, Nk)
+    nqb, nkb = len(q_offsets) - 1, len(k_offsets) - 1
+    heads = {}
+
+    def head(b, h):
+        if (b, h) not in heads:
+            g = h // grp
+            heads.clear()
+            heads[(b, h)] = (_widen(q[b, :, h, :]), _widen(k[b, :, g, :]), _widen(v[b, :, g, :]),
+                             _widen(do[b, :, h, :]), selection_unit(b, h, B, Hq, Hkv, sel_nb, sel_nh))
+        return heads[(b, h)]
+
+    def rows_dq(b, h, toks):
+        qf, kf, vf, dof, unit = head(b, h)
+        out = np.zeros((len(toks), d))
+        for c0 in range(0, len(toks), ROW_CHUNK):
+            t = np.asarray(toks[c0:c0 + ROW_CHUNK], dtype=np.int64)
+            _, dS = _bwd_head_chunk(qf, kf, vf, dof, t, bq, bk, sel_row_ptr, sel_kblk, unit, nqb, nkb, scale,
+                                    causal, q_pos0)
+            out[c0:c0 + len(t)] = scale * (dS @ kf)
+        return out
+
+    def keys_dkdv(b, g, ktoks, qtoks_of_head):
+        ktoks = np.asarray(ktoks, dtype=np.int64)
+        dk = np.zeros((len(ktoks), d))
+        dv = np.zeros((len(ktoks), d))
+        for h in range(g * grp, (g + 1) * grp):
+            qf, kf, vf, dof, unit = head(b, h)
+            toks = qtoks_of_head(h, unit)
+            for c0 in range(0, len(toks), ROW_CHUNK):
+                t = np.asarray(toks[c0:c0 + ROW_CHUNK], dtype=np.int64)
+                p, dS = _bwd_head_chunk(qf, kf, vf, dof, t, bq, bk, sel_row_ptr, sel_kblk, unit, nqb, nkb, scale,
+                                        causal, q_pos0)
+                dv += p[:, ktoks].T @ dof[t]
+                dk += scale * (dS[:, ktoks].T @ qf[t])
+        return dk, dv
+
+    allq = np.arange(Nq, dtype=np.int64)
+    if q_rows is None and k_rows is None:
+        dQ = np.zeros((B, Nq, Hq, d))
+        dK = np.zeros((B, Nk, Hkv, d))
+        dV = np.zeros((B, Nk, Hkv, d))
+        for b in range(B):
+            for h in range(Hq):
+                qf, kf, vf, dof, unit = head(b, h)
+                g = h // grp
+                for c0 in range(0, Nq, ROW_CHUNK):
+                    t = allq[c0:c0 + ROW_CHUNK]
+                    p, dS = _bwd_head_chunk(qf, kf, vf, dof, t, bq, bk, sel_row_ptr, sel_kblk, unit, nqb, nkb,
+                                            scale, causal, q_pos0)
+                    dQ[b, t, h, :] = scale * (dS @ kf)
+                    dV[b, :, g, :] += p.T @ dof[t]
+                    dK[b, :, g, :] += scale * (dS.T @ qf[t])
+        return dQ, dK, dV
+
+    dq_out = [rows_dq(b, h, np.asarray(t)) for (b, h, t) in (q_rows or [])]
+
+    def attending(ktoks):
+        # queries whose graph row holds at least one of ktoks: their Q block selects a K block
+        # of one of the keys (the causal bound is left to the full-row mask)
+        kbs = np.unique(bk[np.asarray(ktoks, dtype=np.int64)])
+
+        def f(h, unit):
+            qbs = [qb for qb in range(nqb)
+                   if np.intersect1d(selected_blocks(sel_row_ptr, sel_kblk, unit * nqb + qb, nkb), kbs).size]
+            return allq[np.isin(bq, np.asarray(qbs, dtype=np.int64))]
+        return f
+
+    dkv_out = [keys_dkdv(b, g, np.asarray(t), attending(t)) for (b, g, t) in (k_rows or [])]
+    return dq_out, dkv_out
+
+
+def masked_attention_bwd_w(w, do, q_rows=None, k_rows=None):
+    """Convenience wrapper for any object carrying the problem's fields."""
+    return masked_attention_bwd(w.q, w.k, w.v, do, w.q_offsets, w.q_perm, w.k_offsets, w.k_perm, w.sel_nb,
+                                w.sel_nh, w.sel_row_ptr, w.sel_kblk, w.scale, w.causal, w.q_pos0,
+                                q_rows=q_rows, k_rows=k_rows)

@@ -58,6 +58,8 @@ class Workload:
     q: Optional[np.ndarray] = None
     k: Optional[np.ndarray] = None
     v: Optional[np.ndarray] = None
+    do: Optional[np.ndarray] = None  # upstream gradient of O (backward only), drawn on demand
+    rng: Optional[np.random.Generator] = dataclasses.field(default=None, repr=False)
 
     @property
     def n_qblocks(self) -> int:
@@ -175,6 +177,17 @@ def _tensors(w: Workload, rng: np.random.Generator) -> None:
     w.q = normal_bf16(rng, (w.B, w.Nq, w.Hq, w.d))
     w.k = normal_bf16(rng, (w.B, w.Nk, w.Hkv, w.d))
     w.v = normal_bf16(rng, (w.B, w.Nk, w.Hkv, w.d))
+    w.rng = rng  # dO, when a backward needs it, continues this stream
+
+
+def draw_dout(w: Workload) -> np.ndarray:
+    """The upstream gradient dO ~ N(0,1) in bf16, shaped like O, drawn once from the
+    workload's generator right after Q, K and V."""
+    if w.do is None:
+        if w.rng is None:
+            raise ValueError("the workload has no tensors")
+        w.do = normal_bf16(w.rng, (w.B, w.Nq, w.Hq, w.d))
+    return w.do
 
 
 def make_cube_workload(name, seed, grid, cube, radius, B, H, d, with_tensors=True) -> Workload:
