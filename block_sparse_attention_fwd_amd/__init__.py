@@ -1,7 +1,7 @@
-"""Python binding of libbsattn: exact block-sparse softmax attention forward on MI355X.
+"""Python binding of libbsattn: exact block-sparse softmax attention on MI355X.
 
-Argument marshalling only.  Every step of the forward pass -- planning (host C++) and
-the attention itself (gfx950 HIP kernels) -- runs inside ``libbsattn.so``; PyTorch is
+Argument marshalling only.  Every step of the forward and backward passes -- planning
+(host C++) and the attention itself (gfx950 HIP kernels) -- runs inside ``libbsattn.so``; PyTorch is
 used here for device memory and streams.  The C entry points keep their C names
 (``bsattn_plan_create``, ``bsattn_fwd``, ...); :class:`Plan` bundles them for tensors.
 
@@ -19,8 +19,8 @@ import numpy as np
 __all__ = [
     "BsattnError", "Problem", "Layout", "Selection", "Stats", "PlanView", "Plan", "library",
     "bsattn_plan_create", "bsattn_plan_device_bytes", "bsattn_plan_upload", "bsattn_plan_stats",
-    "bsattn_plan_export", "bsattn_fwd", "bsattn_fwd_shape", "bsattn_plan_destroy", "bsattn_status_string",
-    "bsattn_last_hip_error", "SHAPE_128x128", "SHAPE_64x256", "PAGE_SIZE",
+    "bsattn_plan_export", "bsattn_fwd", "bsattn_fwd_shape", "bsattn_bwd_workspace_bytes", "bsattn_bwd",
+    "bsattn_plan_destroy", "bsattn_status_string", "bsattn_last_hip_error", "SHAPE_128x128", "SHAPE_64x256", "PAGE_SIZE",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsattn.so")
@@ -76,8 +76,8 @@ class PlanView(ctypes.Structure):
 _lib: Optional[ctypes.CDLL] = None
 
 EXPORTED = ["bsattn_plan_create", "bsattn_plan_device_bytes", "bsattn_plan_upload", "bsattn_plan_stats",
-            "bsattn_plan_export", "bsattn_fwd", "bsattn_fwd_shape", "bsattn_plan_destroy", "bsattn_status_string",
-            "bsattn_last_hip_error"]
+            "bsattn_plan_export", "bsattn_fwd", "bsattn_fwd_shape", "bsattn_bwd_workspace_bytes", "bsattn_bwd",
+            "bsattn_plan_destroy", "bsattn_status_string", "bsattn_last_hip_error"]
 
 
 def library() -> ctypes.CDLL:
@@ -97,6 +97,8 @@ def library() -> ctypes.CDLL:
     lib.bsattn_plan_export.argtypes = [vp, ctypes.POINTER(PlanView)]
     lib.bsattn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp]
     lib.bsattn_fwd_shape.argtypes = [vp, ctypes.c_int32, vp, vp, vp, vp, vp, ctypes.c_float, vp]
+    lib.bsattn_bwd_workspace_bytes.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t)]
+    lib.bsattn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, ctypes.c_size_t, vp]
     lib.bsattn_plan_destroy.argtypes = [vp]
     lib.bsattn_status_string.argtypes = [ctypes.c_int]
     lib.bsattn_status_string.restype = ctypes.c_char_p
@@ -177,6 +179,20 @@ def bsattn_fwd_shape(plan, shape: int, q_ptr: int, k_ptr: int, v_ptr: int, o_ptr
                                       ctypes.c_float(scale), ctypes.c_void_p(stream)), "bsattn_fwd_shape")
 
 
+def bsattn_bwd_workspace_bytes(plan) -> int:
+    n = ctypes.c_size_t()
+    _check(library().bsattn_bwd_workspace_bytes(plan, ctypes.byref(n)), "bsattn_bwd_workspace_bytes")
+    return int(n.value)
+
+
+def bsattn_bwd(plan, q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, do_ptr: int, dq_ptr: int,
+               dk_ptr: int, dv_ptr: int, scale: float, ws_ptr: int, ws_bytes: int, stream: int = 0) -> None:
+    vp = ctypes.c_void_p
+    _check(library().bsattn_bwd(plan, vp(q_ptr), vp(k_ptr), vp(v_ptr), vp(o_ptr), vp(lse_ptr), vp(do_ptr),
+                                vp(dq_ptr), vp(dk_ptr), vp(dv_ptr), ctypes.c_float(scale), vp(ws_ptr), ws_bytes,
+                                vp(stream)), "bsattn_bwd")
+
+
 def bsattn_plan_destroy(plan) -> None:
     _check(library().bsattn_plan_destroy(plan), "bsattn_plan_destroy")
 
@@ -205,7 +221,8 @@ class Plan:
 
     Strides default to contiguous [B, N, H, d] tensors.  ``upload`` binds the plan's
     device tables to a caller-owned device buffer (a torch uint8 tensor is allocated
-    when none is given); ``fwd`` runs the forward pass on torch's current stream.
+    when none is given); ``fwd`` runs the forward pass and ``bwd`` the backward pass on
+    torch's current stream.
     """
 
     def __init__(self, B, Hq, Hkv, Nq, Nk, d, q_offsets, q_perm, k_offsets, k_perm, sel_nb, sel_nh, sel_row_ptr,
@@ -292,3 +309,35 @@ class Plan:
             bsattn_fwd_shape(self.handle, shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                              lse.data_ptr(), scale, stream)
         return o, lse
+
+    def bwd(self, q, k, v, o, lse, do, dq=None, dk=None, dv=None, workspace=None, scale=None, stream=None):
+        """Backward pass: (dQ, dK, dV) for the upstream gradient ``do`` of O, given the
+        forward's ``o`` and ``lse``.  Gradients take the strides of Q, K and V; dO O's."""
+        import torch
+        pr = self.problem
+        if dq is None:
+            dq = torch.empty_strided(q.shape, q.stride(), dtype=torch.bfloat16, device=q.device)
+        if dk is None:
+            dk = torch.empty_strided(k.shape, k.stride(), dtype=torch.bfloat16, device=k.device)
+        if dv is None:
+            dv = torch.empty_strided(v.shape, v.stride(), dtype=torch.bfloat16, device=v.device)
+        for name, t, st in (("q", q, pr.q_stride), ("k", k, pr.k_stride), ("v", v, pr.v_stride),
+                            ("o", o, pr.o_stride), ("do", do, pr.o_stride), ("dq", dq, pr.q_stride),
+                            ("dk", dk, pr.k_stride), ("dv", dv, pr.v_stride)):
+            if t.dtype != torch.bfloat16 or not t.is_cuda:
+                raise BsattnError(1, f"bsattn_bwd: {name} must be a bf16 device tensor")
+            if tuple(t.stride()[:3]) != tuple(st) or t.stride(3) != 1:
+                raise BsattnError(1, f"bsattn_bwd: {name} strides {t.stride()} differ from the plan's")
+        if lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise BsattnError(1, "bsattn_bwd: lse must be contiguous float32 [B, Hq, Nq]")
+        nws = bsattn_bwd_workspace_bytes(self.handle)
+        if workspace is None:
+            workspace = torch.empty(nws, dtype=torch.uint8, device=q.device)
+        if scale is None:
+            scale = 1.0 / float(pr.d) ** 0.5
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        bsattn_bwd(self.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                   do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), scale, workspace.data_ptr(),
+                   workspace.numel() * workspace.element_size(), stream)
+        return dq, dk, dv

@@ -20,7 +20,7 @@ BUILD = os.path.join(PKG, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["plan.cpp", "api.cpp", "fwd_kernel.hip"]
+SOURCES = ["plan.cpp", "api.cpp", "fwd_kernel.hip", "bwd_kernel.hip"]
 # packed-fp32 instructions are kept out of generated code (never emitted by hand either)
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -49,10 +49,10 @@ def build(asm: bool = False, verbose: bool = False) -> str:
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs)
     os.replace(tmp, LIB)
     if asm:
-        cmd = [HIPCC] + HIP_FLAGS + ["-I", INCLUDE, "-I", CSRC, "--cuda-device-only", "-S",
-                                     os.path.join(CSRC, "fwd_kernel.hip"), "-o",
-                                     os.path.join(BUILD, "fwd_kernel.s")]
-        _run(cmd)
+        for k in ("fwd_kernel", "bwd_kernel"):
+            cmd = [HIPCC] + HIP_FLAGS + ["-I", INCLUDE, "-I", CSRC, "--cuda-device-only", "-S",
+                                         os.path.join(CSRC, k + ".hip"), "-o", os.path.join(BUILD, k + ".s")]
+            _run(cmd)
     return LIB
 
 

@@ -1,6 +1,7 @@
 // C-ABI entry points of libbsattn (declared in include/bsattn.h).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <new>
@@ -11,6 +12,7 @@
 
 namespace bsattn {
 hipError_t launch_fwd_shape(const FwdParams& p, int shape, int d, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, int d, hipStream_t stream);
 }
 
 namespace {
@@ -158,7 +160,95 @@ int run_fwd(const bsattn_plan* plan, int sh0, int sh1, const void* q, const void
 }
 }  // namespace
 
+namespace {
+size_t bwd_workspace_bytes(const bsattn_problem& pr) {
+  const size_t n = size_t(pr.B) * size_t(pr.Hq) * size_t(pr.Nq) * sizeof(float);
+  return std::max<size_t>((n + 255) & ~size_t(255), 256);
+}
+
+// Validates the arguments and launches D = rowsum(dO * O), then dK/dV and dQ.
+int run_bwd(const bsattn_plan* plan, const void* q, const void* k, const void* v, const void* o, const float* lse,
+            const void* dout, void* dq, void* dk, void* dv, float scale, void* workspace, size_t workspace_bytes,
+            void* stream) {
+  if (plan == nullptr) return BSATTN_E_ARG;
+  if (plan->dev == nullptr) return BSATTN_E_STATE;
+  const bsattn_problem& pr = plan->prob;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return BSATTN_E_ARG;
+  if (workspace == nullptr || workspace_bytes < bwd_workspace_bytes(pr) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
+    return BSATTN_E_ARG;
+  auto aligned = [](const void* ptr, const int64_t* st) {
+    return ptr != nullptr && (reinterpret_cast<uintptr_t>(ptr) & 15) == 0 && st[0] % 8 == 0 && st[1] % 8 == 0 &&
+           st[2] % 8 == 0 && st[0] >= 0 && st[1] >= 0 && st[2] >= 0;
+  };
+  if (pr.Nq > 0 && (!aligned(q, pr.q_stride) || !aligned(dq, pr.q_stride) || !aligned(o, pr.o_stride) ||
+                    !aligned(dout, pr.o_stride) || lse == nullptr))
+    return BSATTN_E_ARG;
+  if (pr.Nk > 0 && (!aligned(k, pr.k_stride) || !aligned(dk, pr.k_stride) || !aligned(v, pr.v_stride) ||
+                    !aligned(dv, pr.v_stride)))
+    return BSATTN_E_ARG;
+  // rows of one (batch, head) slice are addressed with 32-bit byte offsets
+  auto extent = [&](int32_t n, const int64_t* st) { return n > 0 ? (int64_t(n) - 1) * st[1] * 2 + pr.d * 2 : 0; };
+  const int64_t ext[4] = {extent(pr.Nq, pr.q_stride), extent(pr.Nq, pr.o_stride), extent(pr.Nk, pr.k_stride),
+                          extent(pr.Nk, pr.v_stride)};
+  for (int64_t e : ext)
+    if (e > 0xffffffffLL) return BSATTN_E_UNSUPPORTED;
+  const int64_t n_dq = int64_t(pr.B) * pr.Hq * int64_t(plan->dqt_row0.size());
+  const int64_t n_kv = int64_t(pr.B) * pr.Hkv * int64_t(plan->kvt_row0.size());
+  if (n_dq >= (int64_t(1) << 31) || n_kv >= (int64_t(1) << 31)) return BSATTN_E_UNSUPPORTED;
+
+  const uint8_t* base = static_cast<const uint8_t*>(plan->dev);
+  bsattn::BwdParams bp{};
+  bp.q = q; bp.k = k; bp.v = v; bp.o = o; bp.dout = dout; bp.lse = lse;
+  bp.dq = dq; bp.dk = dk; bp.dv = dv; bp.dvec = static_cast<float*>(workspace);
+  bp.q_sb = pr.q_stride[0]; bp.q_sn = pr.q_stride[1]; bp.q_sh = pr.q_stride[2];
+  bp.k_sb = pr.k_stride[0]; bp.k_sn = pr.k_stride[1]; bp.k_sh = pr.k_stride[2];
+  bp.v_sb = pr.v_stride[0]; bp.v_sn = pr.v_stride[1]; bp.v_sh = pr.v_stride[2];
+  bp.o_sb = pr.o_stride[0]; bp.o_sn = pr.o_stride[1]; bp.o_sh = pr.o_stride[2];
+  bp.dq_tiles = reinterpret_cast<const bsattn::QTileDev*>(base + plan->off_dqt);
+  bp.kv_tiles = reinterpret_cast<const bsattn::QTileDev*>(base + plan->off_kvt);
+  bp.pl_ptr = reinterpret_cast<const int32_t*>(base + plan->off_plptr);
+  bp.pl_ent = reinterpret_cast<const int32_t*>(base + plan->off_plent);
+  bp.tpl_ptr = reinterpret_cast<const int32_t*>(base + plan->off_tplptr);
+  bp.tpl_ent = reinterpret_cast<const int32_t*>(base + plan->off_tplent);
+  bp.qperm = plan->has_qperm ? reinterpret_cast<const int32_t*>(base + plan->off_qperm) : nullptr;
+  bp.kperm = plan->has_kperm ? reinterpret_cast<const int32_t*>(base + plan->off_kperm) : nullptr;
+  bp.q_pos0 = pr.q_pos0;
+  bp.q_extent = uint32_t(ext[0]); bp.o_extent = uint32_t(ext[1]);
+  bp.k_extent = uint32_t(ext[2]); bp.v_extent = uint32_t(ext[3]);
+  bp.q_sn_bytes = uint32_t(pr.q_stride[1] * 2); bp.o_sn_bytes = uint32_t(pr.o_stride[1] * 2);
+  bp.k_sn_bytes = uint32_t(pr.k_stride[1] * 2); bp.v_sn_bytes = uint32_t(pr.v_stride[1] * 2);
+  bp.n_dq_tiles = int32_t(plan->dqt_row0.size());
+  bp.n_kv_tiles = int32_t(plan->kvt_row0.size());
+  bp.B = pr.B; bp.Hq = pr.Hq; bp.Hkv = pr.Hkv; bp.Nq = pr.Nq; bp.Nk = pr.Nk;
+  bp.grp = pr.Hq / pr.Hkv;
+  bp.nqb = plan->nqb;
+  bp.nkb = plan->nkb;
+  bp.sel_nh = plan->sel_nh;
+  bp.ub_mul = (plan->sel_nb == pr.B) ? 1 : 0;
+  bp.uh_div = (plan->sel_nh == pr.Hq) ? 1 : (plan->sel_nh == pr.Hkv ? bp.grp : pr.Hq);
+  bp.causal = pr.causal;
+  bp.scale = scale;
+  bp.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = bsattn::launch_bwd(bp, pr.d, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return BSATTN_OK;
+}
+}  // namespace
+
 extern "C" {
+
+int bsattn_bwd_workspace_bytes(const bsattn_plan* plan, size_t* bytes) {
+  if (plan == nullptr || bytes == nullptr) return BSATTN_E_ARG;
+  *bytes = bwd_workspace_bytes(plan->prob);
+  return BSATTN_OK;
+}
+
+int bsattn_bwd(const bsattn_plan* plan, const void* q, const void* k, const void* v, const void* o,
+               const float* lse, const void* dout, void* dq, void* dk, void* dv, float scale, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  return run_bwd(plan, q, k, v, o, lse, dout, dq, dk, dv, scale, workspace, workspace_bytes, stream);
+}
 
 int bsattn_fwd(const bsattn_plan* plan, const void* q, const void* k, const void* v, void* o, float* lse,
                float scale, void* stream) {

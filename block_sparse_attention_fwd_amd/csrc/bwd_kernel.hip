@@ -1,0 +1,474 @@
+// Exact block-sparse attention backward for gfx950 (MI355X).
+//
+// The gradients are those of masked softmax attention (KPage abstract, zhuanzhiai page 1,
+// sentence 4: exact masking and K/V-owned page packing keep the original sparse graph in
+// backward execution).  With P^ = exp(S - LSE) on the graph's pairs and 0 elsewhere:
+//   D_i   = sum_e dO_ie O_ie                                   (bwd_dot_kernel)
+//   dV_j  = sum_i P^_ij dO_i,  dK_j = scale sum_i dS_ij Q_i    (bwd_dkdv_kernel)
+//   dS_ij = P^_ij (dO_i . V_j - D_i),  dQ_i = scale sum_j dS_ij K_j   (bwd_dq_kernel)
+// summed over the query heads of a KV group for dK and dV.
+//
+// Ownership, no atomics: a dK/dV workgroup owns 64 key slots of one K block (the K/V side
+// of a page never straddles blocks) and walks the transposed page list of that block -- the
+// 16-row Q pages of every Q block that selects it, packed two per 32-query stage across Q
+// block boundaries as they are loaded into LDS.  A dQ workgroup owns 64 query slots of one
+// Q block and walks the forward's K page list of that block, two pages per 32-key stage.
+// Each wave holds 32 owned rows; the owned operands stay in registers and the streamed
+// side comes through LDS.  Every product is v_mfma_f32_32x32x16_bf16 with fp32
+// accumulation; P^ and dS are rounded to bf16 as MFMA operands.
+//
+// Per wave and stage (32 owned x 32 streamed rows, d = 128):
+//   dK/dV:  S = Q K^T, dP = dO V^T  (A = Q, dO rows from LDS; B = K^T, V^T in registers;
+//           each lane gets one key and 16 queries), then
+//           dV^T += dO^T P^, dK^T += Q^T dS  (A = dO^T, Q^T by transposing LDS reads)
+//   dQ:     S^T = K Q^T, dP^T = V dO^T (A = K, V rows; B = Q^T, dO^T in registers), then
+//           dQ^T += K^T dS^T (A = K^T by transposing LDS reads)
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "device_common.hpp"
+#include "kernel_params.hpp"
+
+namespace bsattn {
+
+template <int D>
+struct BwdCfg {
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kChunks = D / 8;              // 16-byte chunks per row
+  static constexpr int kRowsPerInst = 64 / kChunks;  // rows per 64-lane 16-byte load
+  static constexpr int kInst = 16 / kRowsPerInst;    // loads per 16-row page of one tensor
+  static constexpr int kStage = 32 * kRowBytes;      // 32 streamed rows of one tensor
+  static constexpr int kDS = D / 16;                 // k-steps over d
+  static constexpr int kDB = D / 32;                 // 32-wide d blocks of the gradients
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Consecutive work items go to one XCD (one L2): blockIdx x of n items runs item
+// xcd-chunk(x & 7) + (x >> 3).
+__device__ __forceinline__ int xcd_work(int blk, int n) {
+  const int x = blk & 7, i = blk >> 3, q = n >> 3, r = n & 7;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
+}
+
+// causal bound of a query position: a key token is kept iff it is <= the result
+__device__ __forceinline__ int causal_thr(int64_t qpos) {
+  return qpos < -1 ? -1 : (qpos > 0x7ffffffe ? 0x7ffffffe : (int)qpos);
+}
+
+// ---------------------------------------------------------------------------------------
+// D = rowsum(dO * O) in fp32 from the bf16 tensors, one row per D/8 lanes.
+template <int D>
+__global__ void __launch_bounds__(256) bwd_dot_kernel(BwdParams p) {
+  constexpr int L = D / 8;     // lanes per row
+  constexpr int RPW = 64 / L;  // rows per wave
+  const int lane = threadIdx.x & 63;
+  const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / L;
+  const int64_t nrows = (int64_t)p.B * p.Hq * p.Nq;
+  float acc = 0.f;
+  if (row < nrows) {
+    const int64_t bh = row / p.Nq;
+    const int64_t i = row - bh * p.Nq;
+    const int64_t b = bh / p.Hq, h = bh - b * p.Hq;
+    const int64_t off = b * p.o_sb + i * p.o_sn + h * p.o_sh + (lane % L) * 8;
+    const bf16x8 o = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(p.o) + off);
+    const bf16x8 g = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(p.dout) + off);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)o[e], (float)g[e], acc);
+  }
+#pragma unroll
+  for (int m = L / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  if (row < nrows && lane % L == 0) p.dvec[row] = acc;
+}
+
+// ---------------------------------------------------------------------------------------
+// Shared loader: wave w fills rows 16w .. 16w + 15 of a 32-row stage buffer with one 16-row
+// page (first slot, valid rows) of a [tokens, d] slice, gathered through perm when given.
+// Rows past the page's valid count (and a missing page) load the page's first slot: finite
+// data that the masks remove.  Lane (lr, pc) of a load fills physical chunk pc of its row,
+// i.e. logical chunk pc ^ swz(row), so MFMA operand reads are conflict-free.
+template <int D>
+struct PageLoader {
+  using C = BwdCfg<D>;
+  int rip[C::kInst];
+  uint32_t cb[C::kInst];
+  __device__ __forceinline__ void init(int lane) {
+    const int lr = lane / C::kChunks, pc = lane % C::kChunks;
+#pragma unroll
+    for (int n = 0; n < C::kInst; ++n) {
+      rip[n] = n * C::kRowsPerInst + lr;
+      cb[n] = (uint32_t)((pc ^ swz<D>(rip[n])) * 16);
+    }
+  }
+  // one page of two tensors that share the token gather (K and V, or Q and dO)
+  __device__ __forceinline__ void load2(int ent, const int32_t* perm, const __amdgpu_buffer_rsrc_t& ra,
+                                        uint32_t sn_a, uint8_t* dst_a, const __amdgpu_buffer_rsrc_t& rb,
+                                        uint32_t sn_b, uint8_t* dst_b, int wave) const {
+    const int nv = ent_nv(ent), slot0 = ent_slot(ent);
+    uint32_t va[C::kInst], vb[C::kInst];
+#pragma unroll
+    for (int n = 0; n < C::kInst; ++n) {
+      const int slot = slot0 + (rip[n] < nv ? rip[n] : 0);
+      const uint32_t tok = (uint32_t)(perm ? perm[slot] : slot);
+      va[n] = tok * sn_a + cb[n];
+      vb[n] = tok * sn_b + cb[n];
+    }
+#pragma unroll
+    for (int n = 0; n < C::kInst; ++n) {
+      const int row = 16 * wave + n * C::kRowsPerInst;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LDS_AS void*)(dst_a + row * C::kRowBytes), 16, (int)va[n], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (LDS_AS void*)(dst_b + row * C::kRowBytes), 16, (int)vb[n], 0, 0, 0);
+    }
+  }
+};
+
+// A operand of rows `row` (lane % 32) of a stage buffer, k-step s: 8 consecutive d values.
+template <int D>
+__device__ __forceinline__ bf16x8 row_operand(const uint8_t* buf, int lane, int s) {
+  const int r = lane & 31;
+  const int c = (2 * s + (lane >> 5)) ^ swz<D>(r);
+  return *reinterpret_cast<const bf16x8*>(buf + r * BwdCfg<D>::kRowBytes + c * 16);
+}
+
+// A operand of the transposed stage (M = d block db, K = 16 streamed rows of half `half`)
+// in the order of the accumulator layout's rows: lane l takes rows 16 half + 4 (l / 32) +
+// {0..3} and the same + 8, matching a bf16x8 B operand built from accumulator registers
+// 8 half .. 8 half + 7.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const uint8_t* buf, int lane, int half, int db) {
+  using C = BwdCfg<D>;
+  const int v_rr = (lane & 15) >> 2, v_qq = lane & 3, v_dsub = (lane >> 4) & 1;
+  const int ra = 16 * half + 4 * (lane >> 5) + v_rr;
+  const int rb = ra + 8;
+  const int lc = 4 * db + 2 * v_dsub + (v_qq >> 1);
+  const int off_in = (v_qq & 1) * 8;
+  LDS_AS bf16x4* pa = (LDS_AS bf16x4*)(buf + ra * C::kRowBytes + ((lc ^ swz<D>(ra)) * 16) + off_in);
+  LDS_AS bf16x4* pb = (LDS_AS bf16x4*)(buf + rb * C::kRowBytes + ((lc ^ swz<D>(rb)) * 16) + off_in);
+  const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(pa);
+  const bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(pb);
+  return bf16x8{va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+}
+
+// Writes a 32-row x D gradient held transposed in accumulators (lane = row, 16 d values
+// per 32-wide block) as bf16 rows of `dst` (d contiguous), times `mul`.
+template <int D>
+__device__ __forceinline__ void store_rows(__bf16* dst, const f32x16 (&acc)[BwdCfg<D>::kDB], float mul, int lane) {
+  const int hh = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < BwdCfg<D>::kDB; ++db) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bf16x4 v4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v4[j] = (__bf16)(acc[db][4 * i + j] * mul);
+      *reinterpret_cast<bf16x4*>(dst + 32 * db + 8 * i + 4 * hh) = v4;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// dQ: one workgroup (2 waves) per (batch, head, 64-row Q tile).
+template <int D>
+__global__ void __launch_bounds__(128) bwd_dq_kernel(BwdParams p) {
+  using C = BwdCfg<D>;
+  __shared__ __attribute__((aligned(1024))) uint8_t sk[2 * C::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t sv[2 * C::kStage];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hh = lane >> 5;
+  const CONST_AS int32_t* pl_ent = (const CONST_AS int32_t*)p.pl_ent;
+  const CONST_AS int32_t* pl_ptr = (const CONST_AS int32_t*)p.pl_ptr;
+  const CONST_AS int32_t* tiles = (const CONST_AS int32_t*)p.dq_tiles;
+
+  const int work = xcd_work(blockIdx.x, p.B * p.Hq * p.n_dq_tiles);
+  const int bh = work / p.n_dq_tiles;
+  const int t = work - bh * p.n_dq_tiles;
+  const int b = bh / p.Hq, h = bh - b * p.Hq, g = h / p.grp;
+  const int row0 = tiles[4 * t], rows = tiles[4 * t + 1], qblock = tiles[4 * t + 2];
+  const int unit = (b * p.ub_mul) * p.sel_nh + h / p.uh_div;
+  const int lrow = unit * p.nqb + qblock;
+  const int e0 = pl_ptr[lrow], e1 = pl_ptr[lrow + 1];
+  const int ns = (e1 - e0 + 1) >> 1;  // 32-key stages
+
+  // this lane's query: Q^T and dO^T B operands, its LSE (log2 units) and D
+  const int qrow = wave * 32 + (lane & 31);
+  const bool qvalid = qrow < rows;
+  const int qslot = row0 + (qvalid ? qrow : 0);
+  const int qtok = p.qperm ? p.qperm[qslot] : qslot;
+  bf16x8 qreg[C::kDS], goreg[C::kDS];
+  {
+    const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.q_sb + (int64_t)qtok * p.q_sn +
+                       (int64_t)h * p.q_sh + hh * 8;
+    const __bf16* gp = reinterpret_cast<const __bf16*>(p.dout) + (int64_t)b * p.o_sb + (int64_t)qtok * p.o_sn +
+                       (int64_t)h * p.o_sh + hh * 8;
+#pragma unroll
+    for (int s = 0; s < C::kDS; ++s) {
+      qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
+      goreg[s] = *reinterpret_cast<const bf16x8*>(gp + 16 * s);
+    }
+  }
+  const float lse = p.lse[(int64_t)bh * p.Nq + qtok];
+  // a row without keys has LSE = -inf: +inf here makes every probability exp2(-inf) = 0
+  const float lse2 = lse == kNegInf ? __builtin_huge_valf() : lse * kLog2e;
+  const float dval = p.dvec[(int64_t)bh * p.Nq + qtok];
+  const int thr = p.causal ? causal_thr(p.q_pos0 + (int64_t)qtok) : 0x7ffffffe;
+
+  const char* kslice = reinterpret_cast<const char*>(p.k) + ((int64_t)b * p.k_sb + (int64_t)g * p.k_sh) * 2;
+  const char* vslice = reinterpret_cast<const char*>(p.v) + ((int64_t)b * p.v_sb + (int64_t)g * p.v_sh) * 2;
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kslice, (short)0, p.k_extent, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)vslice, (short)0, p.v_extent, 0x00020000);
+  PageLoader<D> ld;
+  ld.init(lane);
+  auto issue = [&](int st, int buf) {
+    const int e = e0 + 2 * st + wave;
+    const int ent = e < e1 ? pl_ent[e] : 0;
+    ld.load2(ent, p.kperm, krsrc, p.k_sn_bytes, sk + buf * C::kStage, vrsrc, p.v_sn_bytes, sv + buf * C::kStage, wave);
+  };
+
+  f32x16 dqacc[C::kDB];
+#pragma unroll
+  for (int db = 0; db < C::kDB; ++db) dqacc[db] = f32x16{};
+  const float sl2 = p.scale_log2;
+
+  if (ns > 0) issue(0, 0);
+  for (int st = 0; st < ns; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < ns) {
+      lds_barrier();  // both waves are done with the other buffer (stage st - 1)
+      issue(st + 1, buf ^ 1);
+      wait_vmcnt<2 * C::kInst>();  // stage st landed; stage st + 1 may be in flight
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();
+    const uint8_t* kb = sk + buf * C::kStage;
+    const uint8_t* vb = sv + buf * C::kStage;
+
+    f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+    for (int s = 0; s < C::kDS; ++s) {
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(kb, lane, s), qreg[s], sacc, 0, 0, 0);
+      dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(vb, lane, s), goreg[s], dpacc, 0, 0, 0);
+    }
+
+    // register i holds key 8 (i / 4) + 4 hh + i % 4 of the stage: page i / 8, row key % 16
+    const int ea = e0 + 2 * st;
+    const int ent0 = pl_ent[ea];
+    const int ent1 = ea + 1 < e1 ? pl_ent[ea + 1] : 0;
+    bf16x8 dsb[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int ent = (i >> 3) ? ent1 : ent0;
+      const int rip = 8 * ((i >> 2) & 1) + 4 * hh + (i & 3);
+      bool keep = rip < ent_nv(ent);
+      if (p.causal) {
+        const int slot = ent_slot(ent) + rip;
+        const int ktok = p.kperm ? p.kperm[keep ? slot : 0] : slot;
+        keep = keep && ktok <= thr;
+      }
+      const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], sl2, -lse2));
+      const float ds = keep ? pr * (dpacc[i] - dval) : 0.f;
+      dsb[i >> 3][i & 7] = (__bf16)ds;
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db)
+        dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(kb, lane, half, db), dsb[half], dqacc[db], 0, 0, 0);
+  }
+
+  if (!qvalid) return;
+  __bf16* dst = reinterpret_cast<__bf16*>(p.dq) + (int64_t)b * p.q_sb + (int64_t)qtok * p.q_sn + (int64_t)h * p.q_sh;
+  store_rows<D>(dst, dqacc, p.scale, lane);
+}
+
+// ---------------------------------------------------------------------------------------
+// dK, dV: one workgroup (2 waves) per (batch, KV head, 64-row K tile); the query heads of
+// the group are walked one after another, each over its unit's transposed page list.
+template <int D>
+__global__ void __launch_bounds__(128) bwd_dkdv_kernel(BwdParams p) {
+  using C = BwdCfg<D>;
+  __shared__ __attribute__((aligned(1024))) uint8_t sq[2 * C::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t sg[2 * C::kStage];
+  __shared__ __attribute__((aligned(16))) float s_lse[2][32];  // LSE in log2 units (+inf: no row)
+  __shared__ __attribute__((aligned(16))) float s_d[2][32];
+  __shared__ __attribute__((aligned(16))) int s_thr[2][32];    // causal bound of each query
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hh = lane >> 5;
+  const CONST_AS int32_t* tpl_ent = (const CONST_AS int32_t*)p.tpl_ent;
+  const CONST_AS int32_t* tpl_ptr = (const CONST_AS int32_t*)p.tpl_ptr;
+  const CONST_AS int32_t* tiles = (const CONST_AS int32_t*)p.kv_tiles;
+
+  const int work = xcd_work(blockIdx.x, p.B * p.Hkv * p.n_kv_tiles);
+  const int bg = work / p.n_kv_tiles;
+  const int t = work - bg * p.n_kv_tiles;
+  const int b = bg / p.Hkv, g = bg - b * p.Hkv;
+  const int slot0 = tiles[4 * t], rows = tiles[4 * t + 1], kblock = tiles[4 * t + 2];
+
+  // this lane's key: K^T and V^T B operands stay in registers
+  const int krow = wave * 32 + (lane & 31);
+  const bool kvalid = krow < rows;
+  const int kslot = slot0 + (kvalid ? krow : 0);
+  const int ktok = p.kperm ? p.kperm[kslot] : kslot;
+  bf16x8 kreg[C::kDS], vreg[C::kDS];
+  {
+    const __bf16* kp = reinterpret_cast<const __bf16*>(p.k) + (int64_t)b * p.k_sb + (int64_t)ktok * p.k_sn +
+                       (int64_t)g * p.k_sh + hh * 8;
+    const __bf16* vp = reinterpret_cast<const __bf16*>(p.v) + (int64_t)b * p.v_sb + (int64_t)ktok * p.v_sn +
+                       (int64_t)g * p.v_sh + hh * 8;
+#pragma unroll
+    for (int s = 0; s < C::kDS; ++s) {
+      kreg[s] = *reinterpret_cast<const bf16x8*>(kp + 16 * s);
+      vreg[s] = *reinterpret_cast<const bf16x8*>(vp + 16 * s);
+    }
+  }
+
+  // stages: for each query head h of the group, ceil(pages / 2) stages of its list
+  auto list_of = [&](int hi, int& a, int& z) {
+    const int h = g * p.grp + hi;
+    const int unit = (b * p.ub_mul) * p.sel_nh + h / p.uh_div;
+    a = tpl_ptr[unit * p.nkb + kblock];
+    z = tpl_ptr[unit * p.nkb + kblock + 1];
+  };
+  int nst = 0;
+  for (int hi = 0; hi < p.grp; ++hi) {
+    int a, z;
+    list_of(hi, a, z);
+    nst += (z - a + 1) >> 1;
+  }
+  // load cursor: head index, next entry, end of its list (uniform)
+  int c_h = 0, c_e = 0, c_z = 0;
+  list_of(0, c_e, c_z);
+  auto skip_empty = [&]() {
+    while (c_e >= c_z && c_h + 1 < p.grp) {
+      ++c_h;
+      list_of(c_h, c_e, c_z);
+    }
+  };
+
+  PageLoader<D> ld;
+  ld.init(lane);
+  // issues the stage at the cursor into buffer buf and returns, in lanes 0..15, the LSE
+  // (log2 units), D and causal bound of the query rows this wave loads
+  auto issue = [&](int buf, float& r_lse, float& r_d, int& r_thr) {
+    skip_empty();
+    const int h = g * p.grp + c_h;
+    const int e = c_e + wave;
+    const int ent = e < c_z ? tpl_ent[e] : 0;
+    // the token of the row whose statistics this lane fetches, before the page loads (a
+    // gather behind them would wait for them)
+    const int nv = ent_nv(ent);
+    const bool valid = lane < nv;
+    const int slot = ent_slot(ent) + (valid ? lane : 0);
+    const int qtok = p.qperm ? p.qperm[slot] : slot;
+    const char* qslice = reinterpret_cast<const char*>(p.q) + ((int64_t)b * p.q_sb + (int64_t)h * p.q_sh) * 2;
+    const char* gslice = reinterpret_cast<const char*>(p.dout) + ((int64_t)b * p.o_sb + (int64_t)h * p.o_sh) * 2;
+    const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)qslice, (short)0, p.q_extent, 0x00020000);
+    const __amdgpu_buffer_rsrc_t grsrc = __builtin_amdgcn_make_buffer_rsrc((void*)gslice, (short)0, p.o_extent, 0x00020000);
+    ld.load2(ent, p.qperm, qrsrc, p.q_sn_bytes, sq + buf * C::kStage, grsrc, p.o_sn_bytes, sg + buf * C::kStage, wave);
+    const int64_t idx = ((int64_t)b * p.Hq + h) * p.Nq + qtok;
+    const float lse = p.lse[idx];
+    r_lse = (valid && lse != kNegInf) ? lse * kLog2e : __builtin_huge_valf();
+    r_d = valid ? p.dvec[idx] : 0.f;
+    r_thr = causal_thr(p.q_pos0 + (int64_t)qtok);
+    c_e += 2;
+  };
+
+  f32x16 dkacc[C::kDB], dvacc[C::kDB];
+#pragma unroll
+  for (int db = 0; db < C::kDB; ++db) {
+    dkacc[db] = f32x16{};
+    dvacc[db] = f32x16{};
+  }
+  const float sl2 = p.scale_log2;
+
+  float n_lse = 0.f, n_d = 0.f;
+  int n_thr = 0;
+  if (nst > 0) issue(0, n_lse, n_d, n_thr);
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    const float c_lse = n_lse, c_d = n_d;
+    const int c_thr = n_thr;
+    if (st + 1 < nst) {
+      lds_barrier();  // both waves are done with the other buffer (stage st - 1)
+      issue(buf ^ 1, n_lse, n_d, n_thr);
+      wait_vmcnt<2 * C::kInst>();  // stage st landed
+    } else {
+      wait_vmcnt<0>();
+    }
+    if (lane < 16) {
+      s_lse[buf][16 * wave + lane] = c_lse;
+      s_d[buf][16 * wave + lane] = c_d;
+      s_thr[buf][16 * wave + lane] = c_thr;
+    }
+    lds_barrier();
+    const uint8_t* qb = sq + buf * C::kStage;
+    const uint8_t* gb = sg + buf * C::kStage;
+
+    f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+    for (int s = 0; s < C::kDS; ++s) {
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(qb, lane, s), kreg[s], sacc, 0, 0, 0);
+      dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(gb, lane, s), vreg[s], dpacc, 0, 0, 0);
+    }
+
+    // register i holds query 8 (i / 4) + 4 hh + i % 4 of the stage and this lane's key
+    bf16x8 pb[2], dsb[2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 l4 = *reinterpret_cast<const float4*>(&s_lse[buf][8 * j + 4 * hh]);
+      const float4 d4 = *reinterpret_cast<const float4*>(&s_d[buf][8 * j + 4 * hh]);
+      int4 t4 = make_int4(0x7ffffffe, 0x7ffffffe, 0x7ffffffe, 0x7ffffffe);
+      if (p.causal) t4 = *reinterpret_cast<const int4*>(&s_thr[buf][8 * j + 4 * hh]);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+      const int tv[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * j + e;
+        float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], sl2, -lv[e]));
+        pr = ktok <= tv[e] ? pr : 0.f;
+        const float ds = pr * (dpacc[i] - dv[e]);
+        pb[i >> 3][i & 7] = (__bf16)pr;
+        dsb[i >> 3][i & 7] = (__bf16)ds;
+      }
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db) {
+        dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(gb, lane, half, db), pb[half], dvacc[db], 0, 0, 0);
+        dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(qb, lane, half, db), dsb[half], dkacc[db], 0, 0, 0);
+      }
+  }
+
+  if (!kvalid) return;
+  __bf16* dkp = reinterpret_cast<__bf16*>(p.dk) + (int64_t)b * p.k_sb + (int64_t)ktok * p.k_sn + (int64_t)g * p.k_sh;
+  __bf16* dvp = reinterpret_cast<__bf16*>(p.dv) + (int64_t)b * p.v_sb + (int64_t)ktok * p.v_sn + (int64_t)g * p.v_sh;
+  store_rows<D>(dkp, dkacc, p.scale, lane);
+  store_rows<D>(dvp, dvacc, 1.f, lane);
+}
+
+// ---------------------------------------------------------------------------------------
+template <int D>
+hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
+  const int64_t nrows = (int64_t)p.B * p.Hq * p.Nq;
+  if (nrows > 0) {
+    constexpr int kRowsPerBlock = 4 * (64 / (D / 8));
+    hipLaunchKernelGGL((bwd_dot_kernel<D>), dim3((unsigned)((nrows + kRowsPerBlock - 1) / kRowsPerBlock)), dim3(256),
+                       0, stream, p);
+  }
+  const int64_t n_kv = (int64_t)p.B * p.Hkv * p.n_kv_tiles;
+  if (n_kv > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)n_kv), dim3(128), 0, stream, p);
+  const int64_t n_dq = (int64_t)p.B * p.Hq * p.n_dq_tiles;
+  if (n_dq > 0) hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)n_dq), dim3(128), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdParams& p, int d, hipStream_t stream) {
+  return d == 128 ? launch_bwd_d<128>(p, stream) : launch_bwd_d<64>(p, stream);
+}
+
+}  // namespace bsattn

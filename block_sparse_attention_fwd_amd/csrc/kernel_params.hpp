@@ -1,4 +1,4 @@
-// Arguments of the forward kernels (passed by value) and the device Q-tile record.
+// Arguments of the forward and backward kernels (passed by value) and the device tile record.
 #pragma once
 
 #include <cstdint>
@@ -35,6 +35,41 @@ struct FwdParams {
   int32_t n_work;             // n_qtiles * B * Hq
   int32_t B, Hq, Hkv, Nq, Nk, grp;
   int32_t nqb, sel_nh, ub_mul, uh_div;
+  int32_t causal;
+  float scale, scale_log2;
+};
+
+// Backward.  Gradients share the layout of their tensors: dO uses O's strides, dQ Q's, dK
+// K's and dV V's.  D = rowsum(dO * O) lives in a float32 [B, Hq, Nq] workspace.
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;  // [B, Hq, Nq], natural log
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dvec;       // workspace: D [B, Hq, Nq]
+  int64_t q_sb, q_sn, q_sh;
+  int64_t k_sb, k_sn, k_sh;
+  int64_t v_sb, v_sn, v_sh;
+  int64_t o_sb, o_sn, o_sh;
+  const QTileDev* dq_tiles;   // 64-row Q tiles (row0, rows, qblock)
+  const QTileDev* kv_tiles;   // 64-row K tiles (first slot, rows, kblock)
+  const int32_t* pl_ptr;      // K pages per (unit, Q block), as in the forward
+  const int32_t* pl_ent;
+  const int32_t* tpl_ptr;     // Q pages per (unit, K block): [n_units * nkb + 1]
+  const int32_t* tpl_ent;     // packed (first slot << 5) | valid rows
+  const int32_t* qperm;
+  const int32_t* kperm;
+  int64_t q_pos0;
+  uint32_t q_extent, o_extent, k_extent, v_extent;  // bytes of one (batch, head) slice
+  uint32_t q_sn_bytes, o_sn_bytes, k_sn_bytes, v_sn_bytes;
+  int32_t n_dq_tiles, n_kv_tiles;
+  int32_t B, Hq, Hkv, Nq, Nk, grp;
+  int32_t nqb, nkb, sel_nh, ub_mul, uh_div;
   int32_t causal;
   float scale, scale_log2;
 };

@@ -198,6 +198,45 @@ int build_plan(const bsattn_problem& prob, const bsattn_layout& ql, const bsattn
   p->stats.page_list_len = int64_t(p->pl_pages.size());
   p->stats.n_units = n_units;
 
+  // backward tables.  Q pages: a Q block of n slots has ceil(n/16) pages, like the K side.
+  // 64-row tiles of each side (a block of n slots gives ceil(n/64) tiles, the last one short).
+  // Transposed lists: for each (unit, K block), the Q pages of every Q block that selects
+  // it -- Q blocks ascending, pages ascending -- so the K/V tile that owns a key walks
+  // exactly the queries in the graph with it (KPage abstract, sentence 4: K/V-owned pages in
+  // backward execution).
+  std::vector<int32_t> first_qpage(size_t(nqb) + 1, 0);
+  for (int32_t qb = 0; qb < nqb; ++qb) {
+    const int32_t s0 = ql.offsets[qb], n = ql.offsets[qb + 1] - s0;
+    for (int32_t pg = 0; pg * kPage < n; ++pg) {
+      p->qpage_qblock.push_back(qb);
+      p->qpage_slot0.push_back(s0 + pg * kPage);
+      p->qpage_nvalid.push_back(std::min(kPage, n - pg * kPage));
+    }
+    first_qpage[qb + 1] = int32_t(p->qpage_qblock.size());
+    for (int32_t r = 0; r < n; r += kBwdTileRows) {
+      p->dqt_qblock.push_back(qb); p->dqt_row0.push_back(s0 + r); p->dqt_rows.push_back(std::min(kBwdTileRows, n - r));
+    }
+  }
+  for (int32_t kb = 0; kb < nkb; ++kb) {
+    const int32_t s0 = kl.offsets[kb], n = kl.offsets[kb + 1] - s0;
+    for (int32_t r = 0; r < n; r += kBwdTileRows) {
+      p->kvt_kblock.push_back(kb); p->kvt_row0.push_back(s0 + r); p->kvt_rows.push_back(std::min(kBwdTileRows, n - r));
+    }
+  }
+  {
+    std::vector<std::vector<int32_t>> kq(size_t(n_units) * size_t(nkb));
+    for (int64_t u = 0; u < n_units; ++u)
+      for (int32_t qb = 0; qb < nqb; ++qb)
+        for (int32_t kb : row_blocks[size_t(u * nqb + qb)]) kq[size_t(u) * nkb + kb].push_back(qb);
+    p->tpl_ptr.assign(kq.size() + 1, 0);
+    for (size_t r = 0; r < kq.size(); ++r) {
+      for (int32_t qb : kq[r])
+        for (int32_t pg = first_qpage[qb]; pg < first_qpage[qb + 1]; ++pg) p->tpl_pages.push_back(pg);
+      p->tpl_ptr[r + 1] = int64_t(p->tpl_pages.size());
+    }
+  }
+  if (p->tpl_pages.size() >= (size_t(1) << 31)) return BSATTN_E_UNSUPPORTED;
+
   // device image: Q tiles per shape, page-list pointers, packed page entries, perms
   size_t off = 0;
   for (int sh = 0; sh < kShapes; ++sh) {
@@ -217,6 +256,16 @@ int build_plan(const bsattn_problem& prob, const bsattn_layout& ql, const bsattn
   p->off_kperm = off;
   // zero padding past the key permutation: a kernel reads a page's 16 slots at once
   if (p->has_kperm) off = align256(off + sizeof(int32_t) * (size_t(Nk) + kPermPad));
+  // backward: tiles of each side, transposed list pointers and entries (zero-padded: a
+  // kernel reads a whole stage of entries at once)
+  p->off_dqt = off;
+  off = align256(off + sizeof(QTileDev) * p->dqt_row0.size());
+  p->off_kvt = off;
+  off = align256(off + sizeof(QTileDev) * p->kvt_row0.size());
+  p->off_tplptr = off;
+  off = align256(off + sizeof(int32_t) * p->tpl_ptr.size());
+  p->off_tplent = off;
+  off = align256(off + sizeof(int32_t) * (p->tpl_pages.size() + kEntryPad));
   p->image.assign(std::max<size_t>(off, 256), 0);
 
   uint8_t* img = p->image.data();
@@ -249,6 +298,17 @@ int build_plan(const bsattn_problem& prob, const bsattn_layout& ql, const bsattn
   }
   if (p->has_qperm) std::memcpy(img + p->off_qperm, ql.perm, sizeof(int32_t) * size_t(Nq));
   if (p->has_kperm) std::memcpy(img + p->off_kperm, kl.perm, sizeof(int32_t) * size_t(Nk));
+  QTileDev* dqt = reinterpret_cast<QTileDev*>(img + p->off_dqt);
+  for (size_t t = 0; t < p->dqt_row0.size(); ++t) dqt[t] = QTileDev{p->dqt_row0[t], p->dqt_rows[t], p->dqt_qblock[t], 0};
+  QTileDev* kvt = reinterpret_cast<QTileDev*>(img + p->off_kvt);
+  for (size_t t = 0; t < p->kvt_row0.size(); ++t) kvt[t] = QTileDev{p->kvt_row0[t], p->kvt_rows[t], p->kvt_kblock[t], 0};
+  int32_t* tpp = reinterpret_cast<int32_t*>(img + p->off_tplptr);
+  for (size_t r = 0; r < p->tpl_ptr.size(); ++r) tpp[r] = int32_t(p->tpl_ptr[r]);
+  int32_t* tent = reinterpret_cast<int32_t*>(img + p->off_tplent);
+  for (size_t e = 0; e < p->tpl_pages.size(); ++e) {
+    const int32_t pg = p->tpl_pages[e];
+    tent[e] = (p->qpage_slot0[pg] << kEntryShift) | p->qpage_nvalid[pg];
+  }
   return BSATTN_OK;
 }
 

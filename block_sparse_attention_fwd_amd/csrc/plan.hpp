@@ -30,6 +30,8 @@ constexpr int kStagePages = 4;
 // zero entries after the page lists (kernels read up to 27 entries past a list's end)
 constexpr size_t kEntryPad = 64;
 constexpr size_t kPermPad = 16;
+// backward tiles: 64 rows of one block on either side (two waves of 32 rows)
+constexpr int kBwdTileRows = 64;
 
 }  // namespace bsattn
 
@@ -48,6 +50,14 @@ struct bsattn_plan {
   int32_t n_qt[bsattn::kShapes] = {0, 0};
   size_t off_plptr = 0, off_plent = 0, off_qperm = 0, off_kperm = 0;
   bool has_qperm = false, has_kperm = false;
+  // backward: Q pages (16 valid rows of one Q block), 64-row tiles of each side, and the
+  // transposed lists -- Q pages per (unit, K block), Q blocks ascending, pages ascending
+  std::vector<int32_t> qpage_qblock, qpage_slot0, qpage_nvalid;
+  std::vector<int32_t> dqt_qblock, dqt_row0, dqt_rows;
+  std::vector<int32_t> kvt_kblock, kvt_row0, kvt_rows;
+  std::vector<int64_t> tpl_ptr;
+  std::vector<int32_t> tpl_pages;
+  size_t off_dqt = 0, off_kvt = 0, off_tplptr = 0, off_tplent = 0;
   // bound device buffer (caller-owned)
   void* dev = nullptr;
 };

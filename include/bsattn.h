@@ -1,5 +1,5 @@
 /*
- * bsattn -- exact block-sparse softmax attention forward for AMD MI355X (gfx950).
+ * bsattn -- exact block-sparse softmax attention (forward and backward) for AMD MI355X (gfx950).
  *
  * The operation (KPage abstract, zhuanzhiai page 1, sentences 2-4; FlashAttention
  * entries of the scifaro related-paper lists for the softmax / log-sum-exp convention):
@@ -170,6 +170,33 @@ int bsattn_fwd(const bsattn_plan* plan, const void* q, const void* k, const void
  * and errors as bsattn_fwd; an unknown shape is BSATTN_E_ARG. */
 int bsattn_fwd_shape(const bsattn_plan* plan, int32_t shape, const void* q, const void* k, const void* v,
                      void* o, float* lse, float scale, void* stream);
+
+/* Backward workspace: bytes of device memory bsattn_bwd needs for D = rowsum(dO * O),
+ * float32 [B, Hq, Nq] (a multiple of 256, at least 256). */
+int bsattn_bwd_workspace_bytes(const bsattn_plan* plan, size_t* bytes);
+
+/* The backward pass: gradients of the same masked softmax attention (KPage abstract,
+ * sentence 4: exact masking and K/V-owned pages keep the sparse graph in backward
+ * execution).  With P^ = exp(scale <Q_i, K_j> - LSE_i) on the graph's pairs and 0 elsewhere,
+ * dO the gradient of O and D_i = sum_e dO_ie O_ie:
+ *     dV[b, j, g, :] = sum over the query heads h of group g, sum_i P^_ij dO[b, i, h, :]
+ *     dS_ij          = P^_ij (<dO[b, i, h, :], V[b, j, g, :]> - D_i)
+ *     dQ[b, i, h, :] = scale sum_j dS_ij K[b, j, g, :]
+ *     dK[b, j, g, :] = scale sum over h of group g, sum_i dS_ij Q[b, i, h, :]
+ * Inputs: q, k, v as for bsattn_fwd; o and lse as bsattn_fwd wrote them for the same
+ * inputs; dout: bf16 dO laid out with O's strides.  Outputs (bf16, fully overwritten): dq
+ * with Q's strides, dk with K's, dv with V's; keys that no query reaches and queries with no
+ * key get zeros.  workspace: caller-owned device memory of at least
+ * bsattn_bwd_workspace_bytes bytes (16-byte aligned), overwritten.  Each dK/dV row is
+ * produced by the one workgroup that owns its key, each dQ row by the one that owns its
+ * query: no atomics, and the result is the same on every call.  Asynchronous on stream; no
+ * allocation, no synchronisation.  The Q and dO rows of one (batch, query head) must lie
+ * within 4 GiB of the slice's first element, like K and V (BSATTN_E_UNSUPPORTED
+ * otherwise).  Q, K, V and dO must be finite in every row of their layouts.  Errors as for
+ * bsattn_fwd; a missing or short workspace is BSATTN_E_ARG. */
+int bsattn_bwd(const bsattn_plan* plan, const void* q, const void* k, const void* v, const void* o,
+               const float* lse, const void* dout, void* dq, void* dk, void* dv, float scale,
+               void* workspace, size_t workspace_bytes, void* stream);
 
 int bsattn_plan_destroy(bsattn_plan* plan);
 

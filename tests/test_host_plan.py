@@ -129,6 +129,16 @@ def test_fwd_before_upload_is_state_error():
     assert e.value.status == 1
 
 
+def test_bwd_before_upload_is_state_error_and_workspace_size():
+    w = make_random(4, B=2, Hq=4, Hkv=2, Nq=40, Nk=50, d=64, with_tensors=False)
+    p = bs.Plan.from_workload(w)
+    # D = rowsum(dO * O): float32 [B, Hq, Nq], rounded up to 256 bytes
+    assert bs.bsattn_bwd_workspace_bytes(p.handle) == 1280
+    with pytest.raises(bs.BsattnError) as e:
+        bs.bsattn_bwd(p.handle, 16, 16, 16, 16, 16, 16, 16, 16, 16, 0.125, 256, 1 << 20, 0)
+    assert e.value.status == 7
+
+
 def test_library_exports_every_declared_symbol():
     import re
     import os
