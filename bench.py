@@ -10,6 +10,9 @@ Metric: useful-pair TFLOP/s = 4 * d * (query-key pairs of the sparse graph) / st
 The default workload is the video-DiT 3D partial-block case (latent grid 21x45x80,
 cubes 2x8x8, 40 heads, d = 128, sliding-tile window +-1 t, +-2 h, +-2 w in cube units).
 
+With ``--bwd`` a step is one ``bsattn_bwd`` call (D = rowsum(dO * O), then the dK/dV and dQ
+kernels) on the independent Q/K partition workload, counted as 10 * d per useful pair.
+
 Prints one JSON line on stdout; progress goes to stderr.
 """
 import argparse
@@ -79,13 +82,96 @@ def cpu_baseline(w, seconds):
                       f"({useful} useful pairs, {t_total:.1f} s)"}
 
 
+def cpu_baseline_bwd(w, do, seconds):
+    """The float64 backward oracle, as it stands, on a bounded sample: dQ of the first query
+    rows of (batch 0, head 0), 256 at a time, until ``seconds`` have passed.  Each such row
+    costs the oracle its scores, probabilities, O, D, dP, dS and dQ over the full key width;
+    the rate counts 10*d per useful pair of the sampled rows."""
+    from oracle.attention import masked_attention_bwd_w, token_block_map, token_mask
+    cores = len(os.sched_getaffinity(0))
+    bq = token_block_map(w.q_offsets, w.q_perm, w.Nq)
+    bk = token_block_map(w.k_offsets, w.k_perm, w.Nk)
+    useful = rows = 0
+    t_total = 0.0
+    while t_total < seconds and rows < w.Nq:
+        toks = np.arange(rows, min(rows + 256, w.Nq))
+        t0 = time.perf_counter()
+        masked_attention_bwd_w(w, do, q_rows=[(0, 0, toks)])
+        t_total += time.perf_counter() - t0
+        m = token_mask(bq, bk, w.sel_row_ptr, w.sel_kblk, 0, w.n_qblocks, w.n_kblocks, toks, w.causal, w.q_pos0)
+        useful += int(m.sum())
+        rows += len(toks)
+    return {"value": 10.0 * w.d * useful / t_total / 1e12, "unit": "useful-pair TFLOP/s (10*d per pair)",
+            "cores": cores, "kind": "oracle",
+            "sample": f"float64 backward oracle, dQ of query tokens 0..{rows - 1} of batch 0, head 0 "
+                      f"({useful} useful pairs, {t_total:.1f} s; the dK/dV products are not in the sample)"}
+
+
+def bench_bwd(args, w, plan, st, t_plan, dev):
+    """One step = one bsattn_bwd call (D, then dK/dV, then dQ) on resident inputs, with O and
+    LSE from one forward call before the timed region."""
+    import torch
+    import block_sparse_attention_fwd_amd as bs
+    from workloads.configs import draw_dout
+
+    def to_dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    do_np = draw_dout(w)
+    q, k, v, do = to_dev(w.q), to_dev(w.k), to_dev(w.v), to_dev(do_np)
+    o, lse = plan.fwd(q, k, v, scale=w.scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nws = bs.bsattn_bwd_workspace_bytes(plan.handle)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(), dq.data_ptr(),
+            dk.data_ptr(), dv.data_ptr(), float(w.scale), ws.data_ptr(), nws, stream.cuda_stream)
+    for _ in range(args.warmup):
+        bs.bsattn_bwd(plan.handle, *ptrs)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        events[i][0].record(stream)
+        bs.bsattn_bwd(plan.handle, *ptrs)
+        events[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ev_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    log(f"[bench] backward {ms_step:.3f} ms/step (wall), {ev_ms:.3f} ms (events)")
+    flop = 10.0 * w.d * st["useful"]
+    value = flop / (ms_step * 1e-3) / 1e12
+    achieved = flop / (ev_ms * 1e-3) / 1e12
+    cpu = None
+    if args.cpu_seconds > 0:
+        log(f"[bench] timing the CPU backward oracle for about {args.cpu_seconds:.0f} s")
+        cpu = cpu_baseline_bwd(w, do_np, args.cpu_seconds)
+    out = {
+        "metric": "useful-pair backward TFLOP/s (10*d*valid QK pairs/s), % bf16 MFMA peak, 1 GPU",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V/dO; block layout and selection as the workload defines)",
+        "config": {"workload": w.name, "pass": "backward", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq,
+                   "Nk": w.Nk, "d": w.d, "useful_pairs": st["useful"],
+                   "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2), "plan_ms": round(t_plan * 1e3, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": f"bsattn_bwd: bwd_dot + bwd_dkdv<{w.d}> + bwd_dq<{w.d}>", "kernel_ms": round(ev_ms, 4)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=3, help="benchmark workload 1-5 (default 3: video-DiT 3D)")
+    ap.add_argument("--workload", type=int, default=None, help="benchmark workload 1-5 (default 3: video-DiT 3D)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline sample budget (0 = skip)")
+    ap.add_argument("--bwd", action="store_true",
+                    help="time the backward pass instead (default workload then 4: independent Q/K partitions)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB, 5 times (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -109,6 +195,8 @@ def main():
         print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
         return
 
+    if args.workload is None:
+        args.workload = 4 if args.bwd else 3
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.perf_counter()
@@ -121,6 +209,9 @@ def main():
     st = plan.stats
     plan.upload()
     log(f"[bench] plan built in {t_plan * 1e3:.1f} ms: {st}")
+    if args.bwd:
+        bench_bwd(args, w, plan, st, t_plan, dev)
+        return
 
     def to_dev(x):
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)

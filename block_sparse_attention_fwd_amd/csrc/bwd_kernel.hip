@@ -44,6 +44,7 @@ struct BwdCfg {
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Consecutive work items go to one XCD (one L2): blockIdx x of n items runs item
 // xcd-chunk(x & 7) + (x >> 3).
@@ -83,13 +84,21 @@ __global__ void __launch_bounds__(256) bwd_dot_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Shared loader: wave w fills rows 16w .. 16w + 15 of a 32-row stage buffer with one 16-row
-// page (first slot, valid rows) of a [tokens, d] slice, gathered through perm when given.
-// Rows past the page's valid count (and a missing page) load the page's first slot: finite
-// data that the masks remove.  Lane (lr, pc) of a load fills physical chunk pc of its row,
-// i.e. logical chunk pc ^ swz(row), so MFMA operand reads are conflict-free.
+// Stage loads.  Wave w fills rows 16w .. 16w + 15 of a 32-row stage buffer with one 16-row
+// page (first slot, valid rows) of a [tokens, d] slice.  Rows past the page's valid count
+// (and a missing page) load the page's first slot: finite data that the masks remove.  Lane
+// (lr, pc) of a load reads logical chunk pc ^ swz(row) of its row and stores it at physical
+// chunk pc, so a wave's store of one load is a contiguous 1 KiB and the MFMA operand reads
+// are conflict-free.
+//
+// The dK/dV kernel stages pages through registers: the loads of stage st + 2 are issued while
+// stage st is computed and written to LDS in the next stage, so one barrier per stage
+// separates the writes of one buffer from the reads of the other.  The dQ kernel, which keeps
+// two waves per SIMD and has no registers to spare, loads pages straight into LDS one stage
+// ahead.  With a permuted layout the token gather runs one stage ahead of the loads, so no
+// load waits on a gather issued just before it.
 template <int D>
-struct PageLoader {
+struct PageRows {
   using C = BwdCfg<D>;
   int rip[C::kInst];
   uint32_t cb[C::kInst];
@@ -101,25 +110,39 @@ struct PageLoader {
       cb[n] = (uint32_t)((pc ^ swz<D>(rip[n])) * 16);
     }
   }
-  // one page of two tensors that share the token gather (K and V, or Q and dO)
-  __device__ __forceinline__ void load2(int ent, const int32_t* perm, const __amdgpu_buffer_rsrc_t& ra,
-                                        uint32_t sn_a, uint8_t* dst_a, const __amdgpu_buffer_rsrc_t& rb,
-                                        uint32_t sn_b, uint8_t* dst_b, int wave) const {
+  // tokens of the rows this lane loads for page entry ent (through perm when PERM)
+  template <bool PERM>
+  __device__ __forceinline__ void gather(int ent, const int32_t* perm, uint32_t (&tok)[C::kInst]) const {
     const int nv = ent_nv(ent), slot0 = ent_slot(ent);
-    uint32_t va[C::kInst], vb[C::kInst];
 #pragma unroll
     for (int n = 0; n < C::kInst; ++n) {
       const int slot = slot0 + (rip[n] < nv ? rip[n] : 0);
-      const uint32_t tok = (uint32_t)(perm ? perm[slot] : slot);
-      va[n] = tok * sn_a + cb[n];
-      vb[n] = tok * sn_b + cb[n];
+      tok[n] = (uint32_t)(PERM ? perm[slot] : slot);
     }
+  }
+  __device__ __forceinline__ void load(const uint32_t (&tok)[C::kInst], const __amdgpu_buffer_rsrc_t& rsrc,
+                                       uint32_t sn, u32x4 (&reg)[C::kInst]) const {
+#pragma unroll
+    for (int n = 0; n < C::kInst; ++n)
+      reg[n] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)(tok[n] * sn + cb[n]), 0, 0);
+  }
+  // the page's rows of two tensors that share the tokens, straight into LDS
+  __device__ __forceinline__ void fire(const uint32_t (&tok)[C::kInst], const __amdgpu_buffer_rsrc_t& ra,
+                                       uint32_t sn_a, uint8_t* dst_a, const __amdgpu_buffer_rsrc_t& rb,
+                                       uint32_t sn_b, uint8_t* dst_b, int wave) const {
 #pragma unroll
     for (int n = 0; n < C::kInst; ++n) {
       const int row = 16 * wave + n * C::kRowsPerInst;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LDS_AS void*)(dst_a + row * C::kRowBytes), 16, (int)va[n], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (LDS_AS void*)(dst_b + row * C::kRowBytes), 16, (int)vb[n], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LDS_AS void*)(dst_a + row * C::kRowBytes), 16,
+                                               (int)(tok[n] * sn_a + cb[n]), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (LDS_AS void*)(dst_b + row * C::kRowBytes), 16,
+                                               (int)(tok[n] * sn_b + cb[n]), 0, 0, 0);
     }
+  }
+  __device__ __forceinline__ void store(const u32x4 (&reg)[C::kInst], uint8_t* buf, int wave, int lane) const {
+#pragma unroll
+    for (int n = 0; n < C::kInst; ++n)
+      *reinterpret_cast<u32x4*>(buf + (16 * wave + n * C::kRowsPerInst) * C::kRowBytes + lane * 16) = reg[n];
   }
 };
 
@@ -169,7 +192,7 @@ __device__ __forceinline__ void store_rows(__bf16* dst, const f32x16 (&acc)[BwdC
 
 // ---------------------------------------------------------------------------------------
 // dQ: one workgroup (2 waves) per (batch, head, 64-row Q tile).
-template <int D>
+template <int D, bool KPERM>
 __global__ void __launch_bounds__(128) bwd_dq_kernel(BwdParams p) {
   using C = BwdCfg<D>;
   __shared__ __attribute__((aligned(1024))) uint8_t sk[2 * C::kStage];
@@ -218,26 +241,40 @@ __global__ void __launch_bounds__(128) bwd_dq_kernel(BwdParams p) {
   const char* vslice = reinterpret_cast<const char*>(p.v) + ((int64_t)b * p.v_sb + (int64_t)g * p.v_sh) * 2;
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)kslice, (short)0, p.k_extent, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)vslice, (short)0, p.v_extent, 0x00020000);
-  PageLoader<D> ld;
-  ld.init(lane);
-  auto issue = [&](int st, int buf) {
-    const int e = e0 + 2 * st + wave;
-    const int ent = e < e1 ? pl_ent[e] : 0;
-    ld.load2(ent, p.kperm, krsrc, p.k_sn_bytes, sk + buf * C::kStage, vrsrc, p.v_sn_bytes, sv + buf * C::kStage, wave);
+  PageRows<D> pr;
+  pr.init(lane);
+  uint32_t tok[C::kInst];  // tokens of the next stage to fire
+  int gst = 0;             // stage of the next gather
+  auto gather = [&]() {
+    const int e = e0 + 2 * gst + wave;  // entries past the list read as empty pages
+    pr.template gather<KPERM>(e < e1 ? pl_ent[e] : 0, p.kperm, tok);
+    ++gst;
   };
+  auto fire = [&](int buf) {
+    pr.fire(tok, krsrc, p.k_sn_bytes, sk + buf * C::kStage, vrsrc, p.v_sn_bytes, sv + buf * C::kStage, wave);
+  };
+  // VMEM loads issued after a stage's pages by the time its wait runs: the next stage's
+  // pages and, with a permutation, the gather of the stage after
+  constexpr int kAfter = 2 * C::kInst + (KPERM ? C::kInst : 0);
 
   f32x16 dqacc[C::kDB];
 #pragma unroll
   for (int db = 0; db < C::kDB; ++db) dqacc[db] = f32x16{};
   const float sl2 = p.scale_log2;
 
-  if (ns > 0) issue(0, 0);
+  if (ns > 0) {
+    gather();
+    fire(0);
+    gather();
+  }
   for (int st = 0; st < ns; ++st) {
     const int buf = st & 1;
     if (st + 1 < ns) {
       lds_barrier();  // both waves are done with the other buffer (stage st - 1)
-      issue(st + 1, buf ^ 1);
-      wait_vmcnt<2 * C::kInst>();  // stage st landed; stage st + 1 may be in flight
+      fire(buf ^ 1);  // stage st + 1
+      gather();       // tokens of stage st + 2
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<kAfter>();  // stage st landed
     } else {
       wait_vmcnt<0>();
     }
@@ -264,11 +301,11 @@ __global__ void __launch_bounds__(128) bwd_dq_kernel(BwdParams p) {
       bool keep = rip < ent_nv(ent);
       if (p.causal) {
         const int slot = ent_slot(ent) + rip;
-        const int ktok = p.kperm ? p.kperm[keep ? slot : 0] : slot;
+        const int ktok = KPERM ? p.kperm[keep ? slot : 0] : slot;
         keep = keep && ktok <= thr;
       }
-      const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], sl2, -lse2));
-      const float ds = keep ? pr * (dpacc[i] - dval) : 0.f;
+      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], sl2, -lse2));
+      const float ds = keep ? pv * (dpacc[i] - dval) : 0.f;
       dsb[i >> 3][i & 7] = (__bf16)ds;
     }
 #pragma unroll
@@ -286,7 +323,7 @@ __global__ void __launch_bounds__(128) bwd_dq_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------------------
 // dK, dV: one workgroup (2 waves) per (batch, KV head, 64-row K tile); the query heads of
 // the group are walked one after another, each over its unit's transposed page list.
-template <int D>
+template <int D, bool QPERM>
 __global__ void __launch_bounds__(128) bwd_dkdv_kernel(BwdParams p) {
   using C = BwdCfg<D>;
   __shared__ __attribute__((aligned(1024))) uint8_t sq[2 * C::kStage];
@@ -338,42 +375,59 @@ __global__ void __launch_bounds__(128) bwd_dkdv_kernel(BwdParams p) {
     list_of(hi, a, z);
     nst += (z - a + 1) >> 1;
   }
-  // load cursor: head index, next entry, end of its list (uniform)
+  // gather cursor: head index, next entry, end of its list (uniform); past the last list
+  // it yields empty pages
   int c_h = 0, c_e = 0, c_z = 0;
   list_of(0, c_e, c_z);
-  auto skip_empty = [&]() {
+
+  PageRows<D> pr;
+  pr.init(lane);
+  // the next stage to load: its head, page entry, the tokens of this lane's load rows and
+  // the token of query row lane % 16 of the page (for the row statistics)
+  int n_h = 0, n_ent = 0, n_stok = 0;
+  uint32_t tok[C::kInst];
+  auto gather = [&]() {
     while (c_e >= c_z && c_h + 1 < p.grp) {
       ++c_h;
       list_of(c_h, c_e, c_z);
     }
-  };
-
-  PageLoader<D> ld;
-  ld.init(lane);
-  // issues the stage at the cursor into buffer buf and returns, in lanes 0..15, the LSE
-  // (log2 units), D and causal bound of the query rows this wave loads
-  auto issue = [&](int buf, float& r_lse, float& r_d, int& r_thr) {
-    skip_empty();
-    const int h = g * p.grp + c_h;
+    n_h = c_h;
     const int e = c_e + wave;
-    const int ent = e < c_z ? tpl_ent[e] : 0;
-    // the token of the row whose statistics this lane fetches, before the page loads (a
-    // gather behind them would wait for them)
-    const int nv = ent_nv(ent);
-    const bool valid = lane < nv;
-    const int slot = ent_slot(ent) + (valid ? lane : 0);
-    const int qtok = p.qperm ? p.qperm[slot] : slot;
+    n_ent = e < c_z ? tpl_ent[e] : 0;
+    c_e += 2;
+    pr.template gather<QPERM>(n_ent, p.qperm, tok);
+    const int r = lane & 15;
+    const int slot = ent_slot(n_ent) + (r < ent_nv(n_ent) ? r : 0);
+    n_stok = QPERM ? p.qperm[slot] : slot;
+  };
+  // the loaded stage, not yet in LDS: Q and dO rows and the row statistics
+  u32x4 rq[C::kInst], rg[C::kInst];
+  float r_lse = 0.f, r_d = 0.f;
+  int r_tok = 0, r_nv = 0;
+  auto load = [&]() {
+    const int h = g * p.grp + n_h;
     const char* qslice = reinterpret_cast<const char*>(p.q) + ((int64_t)b * p.q_sb + (int64_t)h * p.q_sh) * 2;
     const char* gslice = reinterpret_cast<const char*>(p.dout) + ((int64_t)b * p.o_sb + (int64_t)h * p.o_sh) * 2;
     const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)qslice, (short)0, p.q_extent, 0x00020000);
     const __amdgpu_buffer_rsrc_t grsrc = __builtin_amdgcn_make_buffer_rsrc((void*)gslice, (short)0, p.o_extent, 0x00020000);
-    ld.load2(ent, p.qperm, qrsrc, p.q_sn_bytes, sq + buf * C::kStage, grsrc, p.o_sn_bytes, sg + buf * C::kStage, wave);
-    const int64_t idx = ((int64_t)b * p.Hq + h) * p.Nq + qtok;
-    const float lse = p.lse[idx];
-    r_lse = (valid && lse != kNegInf) ? lse * kLog2e : __builtin_huge_valf();
-    r_d = valid ? p.dvec[idx] : 0.f;
-    r_thr = causal_thr(p.q_pos0 + (int64_t)qtok);
-    c_e += 2;
+    pr.load(tok, qrsrc, p.q_sn_bytes, rq);
+    pr.load(tok, grsrc, p.o_sn_bytes, rg);
+    const int64_t idx = ((int64_t)b * p.Hq + h) * p.Nq + n_stok;
+    r_lse = p.lse[idx];
+    r_d = p.dvec[idx];
+    r_tok = n_stok;
+    r_nv = ent_nv(n_ent);
+  };
+  // wave w writes rows 16w .. 16w + 15; its lanes 0..15 the statistics of those rows
+  auto store = [&](int buf) {
+    pr.store(rq, sq + buf * C::kStage, wave, lane);
+    pr.store(rg, sg + buf * C::kStage, wave, lane);
+    if (lane < 16) {
+      const bool valid = lane < r_nv;
+      s_lse[buf][16 * wave + lane] = (valid && r_lse != kNegInf) ? r_lse * kLog2e : __builtin_huge_valf();
+      s_d[buf][16 * wave + lane] = valid ? r_d : 0.f;
+      s_thr[buf][16 * wave + lane] = causal_thr(p.q_pos0 + (int64_t)r_tok);
+    }
   };
 
   f32x16 dkacc[C::kDB], dvacc[C::kDB];
@@ -384,26 +438,22 @@ __global__ void __launch_bounds__(128) bwd_dkdv_kernel(BwdParams p) {
   }
   const float sl2 = p.scale_log2;
 
-  float n_lse = 0.f, n_d = 0.f;
-  int n_thr = 0;
-  if (nst > 0) issue(0, n_lse, n_d, n_thr);
+  if (nst > 0) {
+    gather();
+    load();
+    store(0);
+    gather();
+    load();
+    gather();
+  }
   for (int st = 0; st < nst; ++st) {
     const int buf = st & 1;
-    const float c_lse = n_lse, c_d = n_d;
-    const int c_thr = n_thr;
+    lds_barrier();  // stage st is in LDS; both waves are done with the other buffer
     if (st + 1 < nst) {
-      lds_barrier();  // both waves are done with the other buffer (stage st - 1)
-      issue(buf ^ 1, n_lse, n_d, n_thr);
-      wait_vmcnt<2 * C::kInst>();  // stage st landed
-    } else {
-      wait_vmcnt<0>();
+      store(buf ^ 1);  // stage st + 1
+      load();          // stage st + 2
+      gather();        // tokens of stage st + 3
     }
-    if (lane < 16) {
-      s_lse[buf][16 * wave + lane] = c_lse;
-      s_d[buf][16 * wave + lane] = c_d;
-      s_thr[buf][16 * wave + lane] = c_thr;
-    }
-    lds_barrier();
     const uint8_t* qb = sq + buf * C::kStage;
     const uint8_t* gb = sg + buf * C::kStage;
 
@@ -428,10 +478,10 @@ __global__ void __launch_bounds__(128) bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 4 * j + e;
-        float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], sl2, -lv[e]));
-        pr = ktok <= tv[e] ? pr : 0.f;
-        const float ds = pr * (dpacc[i] - dv[e]);
-        pb[i >> 3][i & 7] = (__bf16)pr;
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], sl2, -lv[e]));
+        pv = ktok <= tv[e] ? pv : 0.f;
+        const float ds = pv * (dpacc[i] - dv[e]);
+        pb[i >> 3][i & 7] = (__bf16)pv;
         dsb[i >> 3][i & 7] = (__bf16)ds;
       }
     }
@@ -461,9 +511,19 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
                        0, stream, p);
   }
   const int64_t n_kv = (int64_t)p.B * p.Hkv * p.n_kv_tiles;
-  if (n_kv > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)n_kv), dim3(128), 0, stream, p);
+  if (n_kv > 0) {
+    if (p.qperm)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3((unsigned)n_kv), dim3(128), 0, stream, p);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3((unsigned)n_kv), dim3(128), 0, stream, p);
+  }
   const int64_t n_dq = (int64_t)p.B * p.Hq * p.n_dq_tiles;
-  if (n_dq > 0) hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)n_dq), dim3(128), 0, stream, p);
+  if (n_dq > 0) {
+    if (p.kperm)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)n_dq), dim3(128), 0, stream, p);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)n_dq), dim3(128), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
