@@ -19,8 +19,8 @@ import numpy as np
 __all__ = [
     "BsattnError", "Problem", "Layout", "Selection", "Stats", "PlanView", "Plan", "library",
     "bsattn_plan_create", "bsattn_plan_device_bytes", "bsattn_plan_upload", "bsattn_plan_stats",
-    "bsattn_plan_export", "bsattn_fwd", "bsattn_fwd_shape", "bsattn_bwd_workspace_bytes", "bsattn_bwd",
-    "bsattn_plan_destroy", "bsattn_status_string", "bsattn_last_hip_error", "SHAPE_128x128", "SHAPE_64x256", "PAGE_SIZE",
+    "bsattn_plan_export", "bsattn_plan_export_bwd", "PlanBwdView", "bsattn_fwd", "bsattn_fwd_shape",
+    "bsattn_bwd_workspace_bytes", "bsattn_bwd", "bsattn_plan_destroy", "bsattn_status_string", "bsattn_last_hip_error", "SHAPE_128x128", "SHAPE_64x256", "PAGE_SIZE",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsattn.so")
@@ -73,11 +73,19 @@ class PlanView(ctypes.Structure):
                 ("pl_ptr", _i64p), ("pl_pages", _i32p)]
 
 
+class PlanBwdView(ctypes.Structure):
+    _fields_ = [("n_qpages", ctypes.c_int64), ("qpage_qblock", _i32p), ("qpage_slot0", _i32p),
+                ("qpage_nvalid", _i32p), ("n_dq_tiles", ctypes.c_int64), ("dqt_qblock", _i32p), ("dqt_row0", _i32p),
+                ("dqt_rows", _i32p), ("n_kv_tiles", ctypes.c_int64), ("kvt_kblock", _i32p), ("kvt_row0", _i32p),
+                ("kvt_rows", _i32p), ("n_trows", ctypes.c_int64), ("tpl_ptr", _i64p), ("tpl_pages", _i32p)]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 EXPORTED = ["bsattn_plan_create", "bsattn_plan_device_bytes", "bsattn_plan_upload", "bsattn_plan_stats",
-            "bsattn_plan_export", "bsattn_fwd", "bsattn_fwd_shape", "bsattn_bwd_workspace_bytes", "bsattn_bwd",
-            "bsattn_plan_destroy", "bsattn_status_string", "bsattn_last_hip_error"]
+            "bsattn_plan_export", "bsattn_plan_export_bwd", "bsattn_fwd", "bsattn_fwd_shape",
+            "bsattn_bwd_workspace_bytes", "bsattn_bwd", "bsattn_plan_destroy", "bsattn_status_string",
+            "bsattn_last_hip_error"]
 
 
 def library() -> ctypes.CDLL:
@@ -95,6 +103,7 @@ def library() -> ctypes.CDLL:
     lib.bsattn_plan_upload.argtypes = [vp, vp, ctypes.c_size_t, vp]
     lib.bsattn_plan_stats.argtypes = [vp, ctypes.POINTER(Stats)]
     lib.bsattn_plan_export.argtypes = [vp, ctypes.POINTER(PlanView)]
+    lib.bsattn_plan_export_bwd.argtypes = [vp, ctypes.POINTER(PlanBwdView)]
     lib.bsattn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp]
     lib.bsattn_fwd_shape.argtypes = [vp, ctypes.c_int32, vp, vp, vp, vp, vp, ctypes.c_float, vp]
     lib.bsattn_bwd_workspace_bytes.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t)]
@@ -162,6 +171,27 @@ def bsattn_plan_export(plan) -> dict:
         "qt_row0": arr(v.qt_row0, v.n_qtiles, np.int32), "qt_rows": arr(v.qt_rows, v.n_qtiles, np.int32),
         "qt_shape": arr(v.qt_shape, v.n_qtiles, np.int32), "pl_ptr": arr(v.pl_ptr, v.n_rows + 1, np.int64),
         "pl_pages": arr(v.pl_pages, n_pl, np.int32),
+    }
+
+
+def bsattn_plan_export_bwd(plan) -> dict:
+    v = PlanBwdView()
+    _check(library().bsattn_plan_export_bwd(plan, ctypes.byref(v)), "bsattn_plan_export_bwd")
+
+    def arr(ptr, n, dt):
+        if n == 0:
+            return np.zeros(0, dtype=dt)
+        return np.ctypeslib.as_array(ptr, shape=(n,)).astype(dt, copy=True)
+
+    n_tpl = int(v.tpl_ptr[v.n_trows]) if v.n_trows >= 0 else 0
+    return {
+        "qpage_qblock": arr(v.qpage_qblock, v.n_qpages, np.int32), "qpage_slot0": arr(v.qpage_slot0, v.n_qpages, np.int32),
+        "qpage_nvalid": arr(v.qpage_nvalid, v.n_qpages, np.int32),
+        "dqt_qblock": arr(v.dqt_qblock, v.n_dq_tiles, np.int32), "dqt_row0": arr(v.dqt_row0, v.n_dq_tiles, np.int32),
+        "dqt_rows": arr(v.dqt_rows, v.n_dq_tiles, np.int32),
+        "kvt_kblock": arr(v.kvt_kblock, v.n_kv_tiles, np.int32), "kvt_row0": arr(v.kvt_row0, v.n_kv_tiles, np.int32),
+        "kvt_rows": arr(v.kvt_rows, v.n_kv_tiles, np.int32),
+        "tpl_ptr": arr(v.tpl_ptr, v.n_trows + 1, np.int64), "tpl_pages": arr(v.tpl_pages, n_tpl, np.int32),
     }
 
 
@@ -266,6 +296,9 @@ class Plan:
 
     def export(self) -> dict:
         return bsattn_plan_export(self.handle)
+
+    def export_bwd(self) -> dict:
+        return bsattn_plan_export_bwd(self.handle)
 
     @property
     def device_bytes(self) -> int:

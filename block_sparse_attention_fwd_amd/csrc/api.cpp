@@ -91,6 +91,26 @@ int bsattn_plan_export(const bsattn_plan* plan, bsattn_plan_view* v) {
   return BSATTN_OK;
 }
 
+int bsattn_plan_export_bwd(const bsattn_plan* plan, bsattn_plan_bwd_view* v) {
+  if (plan == nullptr || v == nullptr) return BSATTN_E_ARG;
+  v->n_qpages = int64_t(plan->qpage_qblock.size());
+  v->qpage_qblock = plan->qpage_qblock.data();
+  v->qpage_slot0 = plan->qpage_slot0.data();
+  v->qpage_nvalid = plan->qpage_nvalid.data();
+  v->n_dq_tiles = int64_t(plan->dqt_row0.size());
+  v->dqt_qblock = plan->dqt_qblock.data();
+  v->dqt_row0 = plan->dqt_row0.data();
+  v->dqt_rows = plan->dqt_rows.data();
+  v->n_kv_tiles = int64_t(plan->kvt_row0.size());
+  v->kvt_kblock = plan->kvt_kblock.data();
+  v->kvt_row0 = plan->kvt_row0.data();
+  v->kvt_rows = plan->kvt_rows.data();
+  v->n_trows = int64_t(plan->tpl_ptr.size()) - 1;
+  v->tpl_ptr = plan->tpl_ptr.data();
+  v->tpl_pages = plan->tpl_pages.data();
+  return BSATTN_OK;
+}
+
 }  // extern "C"
 
 namespace {

@@ -128,6 +128,31 @@ typedef struct bsattn_plan_view {
   const int32_t* pl_pages;    /* [pl_ptr[n_rows]] */
 } bsattn_plan_view;
 
+/* Backward tables of a plan (views into plan memory, valid until bsattn_plan_destroy).
+ * Q pages: each Q block of n slots has ceil(n/16) pages of 16 valid rows (the last may be
+ * short), ordered by Q block then page.  Tiles of 64 slots of one block on each side
+ * (ceil(n/64) per block, the last one short), ordered by block then row.  tpl_ptr/tpl_pages
+ * give, for each (unit, K block) row = unit * n_kblocks + kblock, the Q page ids of every Q
+ * block whose selection holds that K block: Q blocks ascending, each block's pages
+ * ascending (KPage abstract, sentence 4: the K/V side owns its rows in backward). */
+typedef struct bsattn_plan_bwd_view {
+  int64_t n_qpages;
+  const int32_t* qpage_qblock;
+  const int32_t* qpage_slot0;  /* first slot of the page in the Q layout */
+  const int32_t* qpage_nvalid; /* 1..16 */
+  int64_t n_dq_tiles;
+  const int32_t* dqt_qblock;
+  const int32_t* dqt_row0;     /* first slot in the Q layout */
+  const int32_t* dqt_rows;     /* 1..64 */
+  int64_t n_kv_tiles;
+  const int32_t* kvt_kblock;
+  const int32_t* kvt_row0;     /* first slot in the K layout */
+  const int32_t* kvt_rows;     /* 1..64 */
+  int64_t n_trows;             /* n_units * n_kblocks */
+  const int64_t* tpl_ptr;      /* [n_trows + 1] */
+  const int32_t* tpl_pages;    /* [tpl_ptr[n_trows]] Q page ids */
+} bsattn_plan_bwd_view;
+
 typedef struct bsattn_plan bsattn_plan;
 
 /* Build a plan on the host: validate, cut K blocks into pages, route Q blocks into
@@ -149,6 +174,9 @@ int bsattn_plan_upload(bsattn_plan* plan, void* dev, size_t bytes, void* stream)
 int bsattn_plan_stats(const bsattn_plan* plan, bsattn_stats* stats);
 
 int bsattn_plan_export(const bsattn_plan* plan, bsattn_plan_view* view);
+
+/* The backward tables (see bsattn_plan_bwd_view), for the bit-exact planner tests. */
+int bsattn_plan_export_bwd(const bsattn_plan* plan, bsattn_plan_bwd_view* view);
 
 /* The forward pass: O and LSE for every (batch, query, head), asynchronously on stream.
  * q, k, v, o: device bf16 tensors laid out as the problem's strides say (16-byte aligned

@@ -12,7 +12,9 @@ Contents
                 that function (dQ, dK, dV) for an upstream gradient of O.
   planner.py    the page / tile plan: 16-row K/V pages owned by one block, Q-block
                 routing between 128x128 and 64x256 tiles, per-(unit, Q block) page
-                lists and the useful / physical query-key pair counts.
+                lists and the useful / physical query-key pair counts; the backward
+                tables (Q pages, 64-slot tiles of each side, Q page lists per
+                (unit, K block)).
 
 Sources (cited by page title and passage):
   * KPage abstract (zhuanzhiai page 1): sentence 2 (16-row K/V pages of valid tokens,
@@ -31,4 +33,4 @@ from .attention import (  # noqa: F401
     bf16_to_f64, token_block_map, selection_unit, selected_blocks, token_mask,
     masked_attention, brute_force_attention, useful_pairs, masked_attention_bwd, masked_attention_bwd_w,
 )
-from .planner import Plan, build_plan  # noqa: F401
+from .planner import Plan, build_plan, BwdPlan, build_bwd_plan  # noqa: F401

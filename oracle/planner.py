@@ -192,3 +192,77 @@ def _useful_subset(q_offsets, q_tokens, k_offsets, k_perm, B, Hq, Hkv, sel_nb, s
 def build_plan_w(w) -> Plan:
     return build_plan(w.B, w.Hq, w.Hkv, w.q_offsets, w.q_perm, w.k_offsets, w.k_perm, w.sel_nb, w.sel_nh,
                       w.sel_row_ptr, w.sel_kblk, w.causal, w.q_pos0)
+
+
+# ----------------------------------------------------------------------------
+# backward tables
+# ----------------------------------------------------------------------------
+# KPage abstract, sentence 4: K/V-owned page packing keeps the sparse graph in backward
+# execution.  Readings: the key side owns its rows -- each K block is cut into 64-slot tiles
+# (ceil(n/64) per block, the last one short) -- and the query side is streamed in 16-row Q
+# pages (a Q block of n slots has ceil(n/16) pages, as the K side in R2).  For each
+# (unit, K block) the Q pages to visit are those of every Q block whose selection row holds
+# that K block, Q blocks ascending and each block's pages ascending.  The dQ side owns
+# 64-slot tiles of each Q block and reuses the forward's page lists (R5).
+BWD_TILE = 64
+
+
+@dataclasses.dataclass
+class BwdPlan:
+    qpage_qblock: np.ndarray
+    qpage_slot0: np.ndarray
+    qpage_nvalid: np.ndarray
+    dqt_qblock: np.ndarray
+    dqt_row0: np.ndarray
+    dqt_rows: np.ndarray
+    kvt_kblock: np.ndarray
+    kvt_row0: np.ndarray
+    kvt_rows: np.ndarray
+    tpl_ptr: np.ndarray   # int64 [n_units * n_kblocks + 1]
+    tpl_pages: np.ndarray
+
+
+def build_bwd_plan(q_offsets, k_offsets, sel_nb, sel_nh, sel_row_ptr, sel_kblk) -> BwdPlan:
+    nqb, nkb = len(q_offsets) - 1, len(k_offsets) - 1
+    qpq, qps, qpn = [], [], []
+    pages_of_qblock = []
+    for qb in range(nqb):
+        s0, n = int(q_offsets[qb]), int(q_offsets[qb + 1] - q_offsets[qb])
+        ids = []
+        for p0 in range(0, n, PAGE):
+            ids.append(len(qpq))
+            qpq.append(qb)
+            qps.append(s0 + p0)
+            qpn.append(min(PAGE, n - p0))
+        pages_of_qblock.append(ids)
+
+    def tiles(offsets):
+        blk, row0, rows = [], [], []
+        for b in range(len(offsets) - 1):
+            s0, n = int(offsets[b]), int(offsets[b + 1] - offsets[b])
+            for r in range(0, n, BWD_TILE):
+                blk.append(b)
+                row0.append(s0 + r)
+                rows.append(min(BWD_TILE, n - r))
+        return blk, row0, rows
+
+    dq = tiles(q_offsets)
+    kv = tiles(k_offsets)
+    n_units = sel_nb * sel_nh
+    ptr = [0]
+    pages = []
+    for u in range(n_units):
+        for kb in range(nkb):
+            for qb in range(nqb):
+                if kb in selected_blocks(sel_row_ptr, sel_kblk, u * nqb + qb, nkb):
+                    pages.extend(pages_of_qblock[qb])
+            ptr.append(len(pages))
+    i32 = lambda a: np.asarray(a, dtype=np.int32)  # noqa: E731
+    return BwdPlan(qpage_qblock=i32(qpq), qpage_slot0=i32(qps), qpage_nvalid=i32(qpn),
+                   dqt_qblock=i32(dq[0]), dqt_row0=i32(dq[1]), dqt_rows=i32(dq[2]),
+                   kvt_kblock=i32(kv[0]), kvt_row0=i32(kv[1]), kvt_rows=i32(kv[2]),
+                   tpl_ptr=np.asarray(ptr, dtype=np.int64), tpl_pages=i32(pages))
+
+
+def build_bwd_plan_w(w) -> BwdPlan:
+    return build_bwd_plan(w.q_offsets, w.k_offsets, w.sel_nb, w.sel_nh, w.sel_row_ptr, w.sel_kblk)

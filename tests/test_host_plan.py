@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import block_sparse_attention_fwd_amd as bs
-from oracle.planner import build_plan_w
+from oracle.planner import build_plan_w, build_bwd_plan_w
 from workloads.configs import make, make_random, make_chunk_gqa
 
 
@@ -32,6 +32,11 @@ def _compare(w):
     assert tuple(st["physical_by_shape"]) == o.physical_by_shape
     assert tuple(st["useful_by_shape"]) == o.useful_by_shape
     assert sum(o.useful_by_shape) == o.useful
+    eb = p.export_bwd()
+    ob = build_bwd_plan_w(w)
+    for name in ("qpage_qblock", "qpage_slot0", "qpage_nvalid", "dqt_qblock", "dqt_row0", "dqt_rows", "kvt_kblock",
+                 "kvt_row0", "kvt_rows", "tpl_ptr", "tpl_pages"):
+        assert np.array_equal(eb[name], getattr(ob, name)), name
     return st
 
 

@@ -184,3 +184,57 @@ def test_cube_physical_independent_derivation():
             width = 128 if rows == 128 else 256
             phys += rows * width * -(-pages // (width // 16))
     assert phys == build_plan_w(w).physical == 485621760
+
+
+# ---------------------------------------------------------------------------
+# backward tables
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", [61, 62, 63, 64])
+def test_bwd_lists_enumerate_graph_transpose(seed):
+    """Brute force over (unit, query slot, key block): the Q page list of (unit, K block)
+    covers exactly the query slots whose Q block selects that K block, each once, in slot
+    order; its pages never straddle Q blocks; the 64-slot tiles of each side partition
+    every block in order."""
+    from oracle.planner import build_bwd_plan_w
+    w = make_random(seed, B=2, Hq=4, Hkv=2, Nq=300, Nk=260, d=64, max_qblock=70, max_kblock=50, density=0.35,
+                    sel_mode="batch-kv", allow_empty=True, unsorted=True, dup=True, with_tensors=False)
+    bp = build_bwd_plan_w(w)
+    nqb, nkb = w.n_qblocks, w.n_kblocks
+    qblk_of_slot = np.repeat(np.arange(nqb), np.diff(w.q_offsets))
+    for u in range(w.sel_nb * w.sel_nh):
+        for kb in range(nkb):
+            row = u * nkb + kb
+            pages = bp.tpl_pages[bp.tpl_ptr[row]:bp.tpl_ptr[row + 1]]
+            slots = []
+            for pg in pages:
+                s0, nv = int(bp.qpage_slot0[pg]), int(bp.qpage_nvalid[pg])
+                assert 1 <= nv <= 16
+                assert np.all(qblk_of_slot[s0:s0 + nv] == bp.qpage_qblock[pg])
+                slots.extend(range(s0, s0 + nv))
+            want = [s for s in range(w.Nq)
+                    if kb in set(w.sel_kblk[w.sel_row_ptr[u * nqb + qblk_of_slot[s]]:
+                                            w.sel_row_ptr[u * nqb + qblk_of_slot[s] + 1]].tolist())]
+            assert slots == want, (u, kb)
+    for offs, blk, row0, rows in ((w.q_offsets, bp.dqt_qblock, bp.dqt_row0, bp.dqt_rows),
+                                  (w.k_offsets, bp.kvt_kblock, bp.kvt_row0, bp.kvt_rows)):
+        covered = []
+        for b, r0, n in zip(blk, row0, rows):
+            assert 1 <= n <= 64 and offs[b] <= r0 and r0 + n <= offs[b + 1]
+            covered.extend(range(r0, r0 + n))
+        assert covered == list(range(int(offs[-1])))
+
+
+@pytest.mark.parametrize("cfg", [1, 3])
+def test_bwd_lists_count_the_forward_useful_pairs(cfg):
+    """Non-causal, one unit: sum over K blocks of (keys in the block) x (query rows of its
+    Q page list) = the forward plan's useful pairs per head (closed form in the golden file)."""
+    from oracle.planner import build_bwd_plan_w
+    w = make(cfg, with_tensors=False)
+    bp = build_bwd_plan_w(w)
+    per_head = 0
+    for kb in range(w.n_kblocks):
+        pages = bp.tpl_pages[bp.tpl_ptr[kb]:bp.tpl_ptr[kb + 1]]
+        per_head += int(w.k_offsets[kb + 1] - w.k_offsets[kb]) * int(bp.qpage_nvalid[pages].sum())
+    g = _load("closed_form_counts.json")
+    key = {1: "tiny3d", 3: "videodit3d"}[cfg]
+    assert per_head * w.Hq == g[key]["useful"]
