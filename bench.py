@@ -10,7 +10,9 @@ Metric: useful-pair TFLOP/s = 4 * d * (query-key pairs of the sparse graph) / st
 The default workload is the video-DiT 3D partial-block case (latent grid 21x45x80,
 cubes 2x8x8, 40 heads, d = 128, sliding-tile window +-1 t, +-2 h, +-2 w in cube units).
 
-With ``--bwd`` a step is one ``bsattn_bwd`` call (D = rowsum(dO * O), then the dK/dV and dQ
+With ``--fixed-tiles`` the plan is the fixed-tile baseline (one 128x128 tile per selected
+block pair, no page packing, no 64x256 routing) -- the ablation of packing on the same
+kernels.  With ``--bwd`` a step is one ``bsattn_bwd`` call (D = rowsum(dO * O), then the dK/dV and dQ
 kernels) on the independent Q/K partition workload, counted as 10 * d per useful pair.
 
 Prints one JSON line on stdout; progress goes to stderr.
@@ -170,6 +172,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=None, help="benchmark workload 1-5 (default 3: video-DiT 3D)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline sample budget (0 = skip)")
+    ap.add_argument("--fixed-tiles", action="store_true",
+                    help="plan with the fixed-tile baseline (one 128x128 tile per selected block pair, no packing)")
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward pass instead (default workload then 4: independent Q/K partitions)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -204,7 +208,7 @@ def main():
     log(f"[bench] workload {w.name}: inputs generated in {time.perf_counter() - t0:.1f} s")
 
     t0 = time.perf_counter()
-    plan = bs.Plan.from_workload(w)
+    plan = bs.Plan.from_workload(w, flags=bs.PLAN_FIXED_TILES if args.fixed_tiles else 0)
     t_plan = time.perf_counter() - t0
     st = plan.stats
     plan.upload()
@@ -280,10 +284,14 @@ def main():
                    "physical_over_useful": round(st["physical"] / max(st["useful"], 1), 4),
                    "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
                    "kernel_ms": {"128x128": round(k128, 4), "64x256": round(k64, 4)},
+                   "plan": "fixed 128x128 tiles per selected block pair (no packing)" if args.fixed_tiles
+                   else "packed pages, routed Q tiles",
                    "plan_ms": round(t_plan * 1e3, 2)},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if args.fixed_tiles:
+        roofline["traffic"] = None  # the counter runs cover the packed plan only
     print(json.dumps(out), flush=True)
 
 

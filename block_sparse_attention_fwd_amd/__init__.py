@@ -18,7 +18,7 @@ import numpy as np
 
 __all__ = [
     "BsattnError", "Problem", "Layout", "Selection", "Stats", "PlanView", "Plan", "library",
-    "bsattn_plan_create", "bsattn_plan_device_bytes", "bsattn_plan_upload", "bsattn_plan_stats",
+    "bsattn_plan_create", "bsattn_plan_create_ex", "PLAN_FIXED_TILES", "bsattn_plan_device_bytes", "bsattn_plan_upload", "bsattn_plan_stats",
     "bsattn_plan_export", "bsattn_plan_export_bwd", "PlanBwdView", "bsattn_fwd", "bsattn_fwd_shape",
     "bsattn_bwd_workspace_bytes", "bsattn_bwd", "bsattn_plan_destroy", "bsattn_status_string", "bsattn_last_hip_error", "SHAPE_128x128", "SHAPE_64x256", "PAGE_SIZE",
 ]
@@ -28,6 +28,7 @@ DTYPE_BF16 = 1
 SHAPE_128x128 = 0
 SHAPE_64x256 = 1
 PAGE_SIZE = 16
+PLAN_FIXED_TILES = 1
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 _i64p = ctypes.POINTER(ctypes.c_int64)
@@ -82,7 +83,7 @@ class PlanBwdView(ctypes.Structure):
 
 _lib: Optional[ctypes.CDLL] = None
 
-EXPORTED = ["bsattn_plan_create", "bsattn_plan_device_bytes", "bsattn_plan_upload", "bsattn_plan_stats",
+EXPORTED = ["bsattn_plan_create", "bsattn_plan_create_ex", "bsattn_plan_device_bytes", "bsattn_plan_upload", "bsattn_plan_stats",
             "bsattn_plan_export", "bsattn_plan_export_bwd", "bsattn_fwd", "bsattn_fwd_shape",
             "bsattn_bwd_workspace_bytes", "bsattn_bwd", "bsattn_plan_destroy", "bsattn_status_string",
             "bsattn_last_hip_error"]
@@ -99,6 +100,9 @@ def library() -> ctypes.CDLL:
     vp = ctypes.c_void_p
     lib.bsattn_plan_create.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(Layout), ctypes.POINTER(Layout),
                                        ctypes.POINTER(Selection), ctypes.c_int32, ctypes.POINTER(vp)]
+    lib.bsattn_plan_create_ex.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(Layout), ctypes.POINTER(Layout),
+                                          ctypes.POINTER(Selection), ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.POINTER(vp)]
     lib.bsattn_plan_device_bytes.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t)]
     lib.bsattn_plan_upload.argtypes = [vp, vp, ctypes.c_size_t, vp]
     lib.bsattn_plan_stats.argtypes = [vp, ctypes.POINTER(Stats)]
@@ -132,6 +136,15 @@ def bsattn_plan_create(problem: Problem, q_layout: Layout, k_layout: Layout, sel
     h = ctypes.c_void_p()
     _check(library().bsattn_plan_create(ctypes.byref(problem), ctypes.byref(q_layout), ctypes.byref(k_layout),
                                         ctypes.byref(selection), page_size, ctypes.byref(h)), "bsattn_plan_create")
+    return h
+
+
+def bsattn_plan_create_ex(problem: Problem, q_layout: Layout, k_layout: Layout, selection: Selection,
+                          page_size: int = PAGE_SIZE, flags: int = 0) -> ctypes.c_void_p:
+    h = ctypes.c_void_p()
+    _check(library().bsattn_plan_create_ex(ctypes.byref(problem), ctypes.byref(q_layout), ctypes.byref(k_layout),
+                                           ctypes.byref(selection), page_size, flags, ctypes.byref(h)),
+           "bsattn_plan_create_ex")
     return h
 
 
@@ -257,7 +270,7 @@ class Plan:
 
     def __init__(self, B, Hq, Hkv, Nq, Nk, d, q_offsets, q_perm, k_offsets, k_perm, sel_nb, sel_nh, sel_row_ptr,
                  sel_kblk, causal=False, q_pos0=0, q_stride=None, k_stride=None, v_stride=None, o_stride=None,
-                 page_size=PAGE_SIZE):
+                 page_size=PAGE_SIZE, flags=0):
         pr = Problem()
         pr.B, pr.Hq, pr.Hkv, pr.Nq, pr.Nk, pr.d = B, Hq, Hkv, Nq, Nk, d
         pr.dtype = DTYPE_BF16
@@ -275,7 +288,7 @@ class Plan:
         ql = Layout(len(qo) - 1, _ptr(qo), _ptr(qp))
         kl = Layout(len(ko) - 1, _ptr(ko), _ptr(kp))
         sel = Selection(sel_nb, sel_nh, _ptr(rp), _ptr(kb) if kb is not None and kb.size else None)
-        self.handle = bsattn_plan_create(pr, ql, kl, sel, page_size)
+        self.handle = bsattn_plan_create_ex(pr, ql, kl, sel, page_size, flags)
         self._keep = None
         self.device_buffer = None
 

@@ -26,9 +26,9 @@ int hip_fail(hipError_t e) {
 
 extern "C" {
 
-int bsattn_plan_create(const bsattn_problem* problem, const bsattn_layout* q_layout,
-                       const bsattn_layout* k_layout, const bsattn_selection* selection,
-                       int32_t page_size, bsattn_plan** out) {
+int bsattn_plan_create_ex(const bsattn_problem* problem, const bsattn_layout* q_layout,
+                          const bsattn_layout* k_layout, const bsattn_selection* selection,
+                          int32_t page_size, int32_t flags, bsattn_plan** out) {
   if (out == nullptr) return BSATTN_E_ARG;
   *out = nullptr;
   if (problem == nullptr || q_layout == nullptr || k_layout == nullptr || selection == nullptr)
@@ -38,7 +38,7 @@ int bsattn_plan_create(const bsattn_problem* problem, const bsattn_layout* q_lay
   if (p == nullptr) return BSATTN_E_OOM;
   int st;
   try {
-    st = bsattn::build_plan(*problem, *q_layout, *k_layout, *selection, p);
+    st = bsattn::build_plan(*problem, *q_layout, *k_layout, *selection, flags, p);
   } catch (const std::bad_alloc&) {
     st = BSATTN_E_OOM;
   } catch (...) {
@@ -50,6 +50,12 @@ int bsattn_plan_create(const bsattn_problem* problem, const bsattn_layout* q_lay
   }
   *out = p;
   return BSATTN_OK;
+}
+
+int bsattn_plan_create(const bsattn_problem* problem, const bsattn_layout* q_layout,
+                       const bsattn_layout* k_layout, const bsattn_selection* selection,
+                       int32_t page_size, bsattn_plan** out) {
+  return bsattn_plan_create_ex(problem, q_layout, k_layout, selection, page_size, 0, out);
 }
 
 int bsattn_plan_device_bytes(const bsattn_plan* plan, size_t* bytes) {

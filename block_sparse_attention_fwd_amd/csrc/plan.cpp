@@ -8,6 +8,10 @@
 //              into ceil(pages / pages-per-tile) tiles of 8 (128x128) or 16 (64x256) pages;
 //   counts     useful = graph pairs; physical = tile rows x tile cols x K tiles, summed
 //              over every (batch, head) and Q tile.
+// With BSATTN_PLAN_FIXED_TILES (the fixed-tile baseline the abstract compares against,
+// sentences 5 and 7): every Q tile has 128 rows (ceil(n/128) per block, no 64-row tiles),
+// and each selected K block starts a new K tile: its pages are followed by empty slots up
+// to a multiple of 8 entries, so no tile packs pages of two blocks.
 #include "plan.hpp"
 
 #include <algorithm>
@@ -42,7 +46,9 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 }  // namespace
 
 int build_plan(const bsattn_problem& prob, const bsattn_layout& ql, const bsattn_layout& kl,
-               const bsattn_selection& sel, bsattn_plan* p) {
+               const bsattn_selection& sel, int32_t flags, bsattn_plan* p) {
+  if ((flags & ~int32_t(BSATTN_PLAN_FIXED_TILES)) != 0) return BSATTN_E_ARG;
+  const bool fixed = (flags & BSATTN_PLAN_FIXED_TILES) != 0;
   const int32_t B = prob.B, Hq = prob.Hq, Hkv = prob.Hkv, Nq = prob.Nq, Nk = prob.Nk;
   if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 0 || Nk < 0 || Hq % Hkv != 0) return BSATTN_E_ARG;
   if (prob.causal != 0 && prob.causal != 1) return BSATTN_E_ARG;
@@ -71,6 +77,7 @@ int build_plan(const bsattn_problem& prob, const bsattn_layout& ql, const bsattn
     if (sel.kblk[e] < 0 || sel.kblk[e] >= nkb) return BSATTN_E_SELECTION;
 
   p->prob = prob;
+  p->flags = flags;
   p->nqb = nqb;
   p->nkb = nkb;
   p->sel_nb = sel.n_b;
@@ -100,7 +107,7 @@ int build_plan(const bsattn_problem& prob, const bsattn_layout& ql, const bsattn
     if (r > 0) {
       p->qt_qblock.push_back(qb); p->qt_row0.push_back(s0 + 128 * full);
       p->qt_rows.push_back(r);
-      p->qt_shape.push_back(r <= 64 ? BSATTN_SHAPE_64x256 : BSATTN_SHAPE_128x128);
+      p->qt_shape.push_back(r <= 64 && !fixed ? BSATTN_SHAPE_64x256 : BSATTN_SHAPE_128x128);
     }
   }
 
@@ -112,8 +119,11 @@ int build_plan(const bsattn_problem& prob, const bsattn_layout& ql, const bsattn
     row_sel.assign(sel.kblk + sel.row_ptr[r], sel.kblk + sel.row_ptr[r + 1]);
     std::sort(row_sel.begin(), row_sel.end());
     row_sel.erase(std::unique(row_sel.begin(), row_sel.end()), row_sel.end());
-    for (int32_t kb : row_sel)
+    for (int32_t kb : row_sel) {
       for (int32_t pg = first_page[kb]; pg < first_page[kb + 1]; ++pg) p->pl_pages.push_back(pg);
+      if (fixed)  // pad the block to whole 8-page tiles with empty slots (page id -1)
+        for (int32_t n = first_page[kb + 1] - first_page[kb]; n % kPagesPerKTile[0] != 0; ++n) p->pl_pages.push_back(-1);
+    }
     p->pl_ptr[r + 1] = int64_t(p->pl_pages.size());
     row_blocks[r] = row_sel;
   }
@@ -282,7 +292,7 @@ int build_plan(const bsattn_problem& prob, const bsattn_layout& ql, const bsattn
   int32_t* ent = reinterpret_cast<int32_t*>(img + p->off_plent);
   for (size_t e = 0; e < p->pl_pages.size(); ++e) {
     const int32_t pg = p->pl_pages[e];
-    ent[e] = (p->page_slot0[pg] << kEntryShift) | p->page_nvalid[pg];
+    ent[e] = pg < 0 ? 0 : (p->page_slot0[pg] << kEntryShift) | p->page_nvalid[pg];  // -1: empty slot
   }
   // mask flag: every entry of a kStagePages-entry stage (counted from its list's start) with
   // a partial page, or cut short by the list's end, carries kEntryMaskBit

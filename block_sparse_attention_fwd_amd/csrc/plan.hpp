@@ -37,6 +37,7 @@ constexpr int kBwdTileRows = 64;
 
 struct bsattn_plan {
   bsattn_problem prob{};
+  int32_t flags = 0;  // BSATTN_PLAN_*
   int32_t nqb = 0, nkb = 0, sel_nb = 1, sel_nh = 1, n_units = 1;
   // canonical arrays (exported)
   std::vector<int32_t> page_kblock, page_slot0, page_nvalid;
@@ -64,6 +65,7 @@ struct bsattn_plan {
 
 namespace bsattn {
 // Builds *p from validated arguments; returns a bsattn_status.
+// flags: BSATTN_PLAN_* (0 = the packed plan)
 int build_plan(const bsattn_problem& prob, const bsattn_layout& ql, const bsattn_layout& kl,
-               const bsattn_selection& sel, bsattn_plan* p);
+               const bsattn_selection& sel, int32_t flags, bsattn_plan* p);
 }  // namespace bsattn

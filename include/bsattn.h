@@ -162,6 +162,23 @@ int bsattn_plan_create(const bsattn_problem* problem, const bsattn_layout* q_lay
                        const bsattn_layout* k_layout, const bsattn_selection* selection,
                        int32_t page_size, bsattn_plan** out);
 
+/* Plan flags for bsattn_plan_create_ex. */
+enum {
+  /* The fixed-tile baseline that page packing and Q routing are measured against (KPage
+   * abstract, sentences 5 and 7: speedup over NVIDIA BSA, physical pair capacity): every
+   * Q tile has 128 rows (no 64x256 routing) and every selected K block starts a new
+   * 128-key tile, padded with empty page slots -- one 128x128 tile per (Q block, selected
+   * K block) pair for blocks of at most 128 tokens.  Same results, more physical pairs. */
+  BSATTN_PLAN_FIXED_TILES = 1
+};
+
+/* bsattn_plan_create with flags (0 gives the same plan as bsattn_plan_create); unknown
+ * flag bits are BSATTN_E_ARG.  In a BSATTN_PLAN_FIXED_TILES plan the exported page lists
+ * hold -1 for the empty padding slots. */
+int bsattn_plan_create_ex(const bsattn_problem* problem, const bsattn_layout* q_layout,
+                          const bsattn_layout* k_layout, const bsattn_selection* selection,
+                          int32_t page_size, int32_t flags, bsattn_plan** out);
+
 /* Bytes of device memory the plan needs (a multiple of 256). */
 int bsattn_plan_device_bytes(const bsattn_plan* plan, size_t* bytes);
 

@@ -20,6 +20,12 @@ Readings of what the abstract leaves open (one per rule):
                  the last K tile may hold empty page slots.  Nothing is pruned for causality.
   R6 counts      useful U = pairs in the graph (causal exclusions removed); physical
                  P = sum over (batch, head) and Q tiles of tile_rows * tile_cols * n_ktiles.
+
+The fixed-tile baseline (``fixed_tiles=True``; the abstract's sentences 5 and 7 measure
+packing and routing against NVIDIA BSA): R4 without the 64-row shape (ceil(n/128) 128-row
+tiles per Q block) and R5 with every selected block starting a new K tile -- its pages are
+followed by empty slots (page id -1) up to a multiple of 8 -- so a tile never holds pages
+of two blocks.
 """
 from __future__ import annotations
 
@@ -74,7 +80,7 @@ class Plan:
 
 
 def build_plan(B, Hq, Hkv, q_offsets, q_perm, k_offsets, k_perm, sel_nb, sel_nh, sel_row_ptr, sel_kblk,
-               causal=False, q_pos0=0, page_size=PAGE) -> Plan:
+               causal=False, q_pos0=0, page_size=PAGE, fixed_tiles=False) -> Plan:
     if page_size != PAGE:
         raise ValueError("only 16-row pages are defined")
     nqb, nkb = len(q_offsets) - 1, len(k_offsets) - 1
@@ -102,8 +108,10 @@ def build_plan(B, Hq, Hkv, q_offsets, q_perm, k_offsets, k_perm, sel_nb, sel_nh,
         full, r = divmod(n, 128)
         for t in range(full):
             qq.append(qb); qr.append(s0 + 128 * t); qn.append(128); qs.append(SHAPE_128x128)
-        if 0 < r <= 64:
+        if 0 < r <= 64 and not fixed_tiles:
             qq.append(qb); qr.append(s0 + 128 * full); qn.append(r); qs.append(SHAPE_64x256)
+        elif 0 < r <= 64:
+            qq.append(qb); qr.append(s0 + 128 * full); qn.append(r); qs.append(SHAPE_128x128)
         elif r > 64:
             qq.append(qb); qr.append(s0 + 128 * full); qn.append(r); qs.append(SHAPE_128x128)
 
@@ -114,6 +122,9 @@ def build_plan(B, Hq, Hkv, q_offsets, q_perm, k_offsets, k_perm, sel_nb, sel_nh,
         for qb in range(nqb):
             for kb in selected_blocks(sel_row_ptr, sel_kblk, u * nqb + qb, nkb):
                 pl.extend(range(first_page[kb], first_page[kb + 1]))
+                if fixed_tiles:
+                    npg = first_page[kb + 1] - first_page[kb]
+                    pl.extend([-1] * (-npg % PAGES_PER_KTILE[SHAPE_128x128]))
             pl_ptr.append(len(pl))
     pl_ptr = np.asarray(pl_ptr, dtype=np.int64)
 
@@ -189,9 +200,9 @@ def _useful_subset(q_offsets, q_tokens, k_offsets, k_perm, B, Hq, Hkv, sel_nb, s
     return total
 
 
-def build_plan_w(w) -> Plan:
+def build_plan_w(w, fixed_tiles=False) -> Plan:
     return build_plan(w.B, w.Hq, w.Hkv, w.q_offsets, w.q_perm, w.k_offsets, w.k_perm, w.sel_nb, w.sel_nh,
-                      w.sel_row_ptr, w.sel_kblk, w.causal, w.q_pos0)
+                      w.sel_row_ptr, w.sel_kblk, w.causal, w.q_pos0, fixed_tiles=fixed_tiles)
 
 
 # ----------------------------------------------------------------------------

@@ -115,6 +115,21 @@ def test_random_full(kw):
     check_full(make_random(**kw), f"random-{kw['seed']}")
 
 
+@pytest.mark.parametrize("case", ["tiny3d", "seed103", "seed105"])
+def test_fixed_tiles_plan_same_results(case):
+    # the fixed-tile baseline plan (no packing, no 64-row routing) runs the same kernels
+    # with padded page slots and must give the same results
+    if case == "tiny3d":
+        w = make(1)
+    else:
+        w = make_random(**[c for c in RANDOM_CASES if f"seed{c['seed']}" == case][0])
+    _say(f"[gpu] fixed-tile plan {case}: Nq={w.Nq} Nk={w.Nk} d={w.d} causal={w.causal}")
+    plan = bs.Plan.from_workload(w, flags=bs.PLAN_FIXED_TILES).upload()
+    O, L, _ = run_gpu(w, plan=plan)
+    Or, Lr = masked_attention_w(w)
+    check_rows(np.transpose(O, (0, 2, 1, 3)), L, np.transpose(Or, (0, 2, 1, 3)), Lr, f"fixed-{case}")
+
+
 def test_empty_rows_and_empty_selection():
     # no Q block selects anything: every row has no key
     w = make_random(111, B=1, Hq=2, Hkv=2, Nq=200, Nk=300, d=128, max_qblock=90, max_kblock=50, sel_mode="head")

@@ -15,11 +15,11 @@ from oracle.planner import build_plan_w, build_bwd_plan_w
 from workloads.configs import make, make_random, make_chunk_gqa
 
 
-def _compare(w):
-    p = bs.Plan.from_workload(w)
+def _compare(w, flags=0):
+    p = bs.Plan.from_workload(w, flags=flags)
     ex = p.export()
     st = p.stats
-    o = build_plan_w(w)
+    o = build_plan_w(w, fixed_tiles=bool(flags & bs.PLAN_FIXED_TILES))
     for name in ("page_kblock", "page_slot0", "page_nvalid", "qt_qblock", "qt_row0", "qt_rows", "qt_shape",
                  "pl_ptr", "pl_pages"):
         assert np.array_equal(ex[name], getattr(o, name)), name
@@ -51,6 +51,18 @@ def test_chunk_gqa_scaled_bit_exact():
     assert st["useful"] < 2 * 8 * 512 * 120 * 64  # causal exclusions removed
 
 
+@pytest.mark.parametrize("cfg", [1, 3, 4])
+def test_fixed_tiles_bit_exact(cfg):
+    _compare(make(cfg, with_tensors=False), flags=bs.PLAN_FIXED_TILES)
+
+
+def test_unknown_plan_flag_is_arg_error():
+    w = make_random(5, Nq=40, Nk=40, d=64, with_tensors=False)
+    with pytest.raises(bs.BsattnError) as e:
+        bs.Plan.from_workload(w, flags=2)
+    assert e.value.status == 1
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_random_bit_exact(seed):
     rng = np.random.default_rng(1000 + seed)
@@ -62,7 +74,7 @@ def test_random_bit_exact(seed):
               sel_mode=str(rng.choice(["shared", "kv", "head", "batch-kv"])), allow_empty=bool(rng.random() < 0.4),
               use_perm=bool(rng.random() < 0.4), causal=bool(rng.random() < 0.4), unsorted=bool(rng.random() < 0.3),
               dup=bool(rng.random() < 0.3), with_tensors=False)
-    _compare(make_random(2000 + seed, **kw))
+    _compare(make_random(2000 + seed, **kw), flags=int(rng.random() < 0.3))
 
 
 def _problem(B=1, Hq=1, Hkv=1, Nq=4, Nk=4, d=64):

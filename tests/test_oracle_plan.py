@@ -238,3 +238,18 @@ def test_bwd_lists_count_the_forward_useful_pairs(cfg):
     g = _load("closed_form_counts.json")
     key = {1: "tiny3d", 3: "videodit3d"}[cfg]
     assert per_head * w.Hq == g[key]["useful"]
+
+
+@pytest.mark.parametrize("cfg,key", [(1, "tiny3d"), (3, "videodit3d")])
+def test_fixed_tiles_closed_form(cfg, key):
+    """Fixed-tile baseline on blocks of at most 128 tokens: one 128x128 tile per (Q block,
+    selected K block) pair, so physical = 16384 x block pairs x heads (block pairs from the
+    per-axis closed form); the useful pairs are those of the packed plan."""
+    g = _load("closed_form_counts.json")[key]
+    w = make(cfg, with_tensors=False)
+    fx = build_plan_w(w, fixed_tiles=True)
+    assert fx.physical == 128 * 128 * g["block_pairs"] * g["heads"]
+    assert fx.useful == g["useful"]
+    assert fx.n_qtiles64 == 0
+    ratio = fx.physical / fx.useful
+    assert abs(ratio - {1: 9.4815, 3: 1.1620}[cfg]) < 1e-4
