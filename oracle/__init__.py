@@ -15,6 +15,8 @@ Contents
                 lists and the useful / physical query-key pair counts; the backward
                 tables (Q pages, 64-slot tiles of each side, Q page lists per
                 (unit, K block)).
+  chunk_index.py  chunk selection: mean-key chunk summaries, one indexing query per
+                KV group, top-k chunks (CISA abstract, sentences 3-5).
 
 Sources (cited by page title and passage):
   * KPage abstract (zhuanzhiai page 1): sentence 2 (16-row K/V pages of valid tokens,
@@ -34,3 +36,4 @@ from .attention import (  # noqa: F401
     masked_attention, brute_force_attention, useful_pairs, masked_attention_bwd, masked_attention_bwd_w,
 )
 from .planner import Plan, build_plan, BwdPlan, build_bwd_plan  # noqa: F401
+from .chunk_index import chunk_summaries, indexing_queries, chunk_scores, select_chunks  # noqa: F401
