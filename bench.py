@@ -12,7 +12,9 @@ cubes 2x8x8, 40 heads, d = 128, sliding-tile window +-1 t, +-2 h, +-2 w in cube 
 
 With ``--fixed-tiles`` the plan is the fixed-tile baseline (one 128x128 tile per selected
 block pair, no page packing, no 64x256 routing) -- the ablation of packing on the same
-kernels.  With ``--bwd`` a step is one ``bsattn_bwd`` call (D = rowsum(dO * O), then the dK/dV and dQ
+kernels.  With ``--chunk-select`` a step is one ``bsattn_chunk_select`` call (chunk
+summaries and top-k chunks of the chunk-indexed prefill workload; HBM-bound, reported in
+GB/s).  With ``--bwd`` a step is one ``bsattn_bwd`` call (D = rowsum(dO * O), then the dK/dV and dQ
 kernels) on the independent Q/K partition workload, counted as 10 * d per useful pair.
 
 Prints one JSON line on stdout; progress goes to stderr.
@@ -165,6 +167,61 @@ def bench_bwd(args, w, plan, st, t_plan, dev):
     print(json.dumps(out), flush=True)
 
 
+def bench_chunk_select(args, w, dev):
+    """One step = one bsattn_chunk_select call (chunk summaries, then the top-k per
+    (batch, KV group)) on the chunk-indexed prefill shapes; HBM-bound: K is read once."""
+    import torch
+    import block_sparse_attention_fwd_amd as bs
+
+    def to_dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    chunk, topk = int(w.k_offsets[1] - w.k_offsets[0]), int(w.sel_row_ptr[1] - w.sel_row_ptr[0])
+    q, k = to_dev(w.q), to_dev(w.k)
+    summ, chunks = bs.chunk_select(q, k, w.Hkv, chunk, topk)
+    torch.cuda.synchronize()
+    pr = bs.ChunkProblem()
+    pr.B, pr.Hq, pr.Hkv, pr.Nq, pr.Nk, pr.d = w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d
+    pr.chunk, pr.topk, pr.query_index, pr.reserved = chunk, topk, w.Nq - 1, 0
+    pr.q_stride[:] = tuple(q.stride()[:3])
+    pr.k_stride[:] = tuple(k.stride()[:3])
+    stream = torch.cuda.current_stream()
+    ptrs = (q.data_ptr(), k.data_ptr(), summ.data_ptr(), chunks.data_ptr(), stream.cuda_stream)
+    for _ in range(args.warmup):
+        bs.bsattn_chunk_select(pr, *ptrs)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        events[i][0].record(stream)
+        bs.bsattn_chunk_select(pr, *ptrs)
+        events[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ev_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    n = summ.shape[2]
+    # algorithmic bytes: K once, the summaries written and read back once, the chunk ids
+    nbytes = w.B * w.Nk * w.Hkv * w.d * 2 + 2 * w.B * w.Hkv * n * w.d * 4 + w.B * w.Hkv * topk * 4
+    same = bool(np.array_equal(chunks.cpu().numpy().reshape(w.B * w.Hkv, topk),
+                               w.sel_kblk.reshape(w.B * w.Hkv, topk)))
+    log(f"[bench] chunk selection {ms_step:.3f} ms/step (wall), {ev_ms:.3f} ms (events); "
+        f"same chunks as the workload's own selection: {same}")
+    out = {
+        "metric": "chunk selection HBM GB/s (K read once + summaries), 1 GPU",
+        "value": round(nbytes / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K)",
+        "config": {"workload": w.name, "pass": "chunk selection", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq,
+                   "Nk": w.Nk, "d": w.d, "chunk": chunk, "topk": topk, "n_chunks": n, "bytes": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / (ev_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(nbytes / (ev_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": f"chunk_summary_kernel<{w.d}> + chunk_topk_kernel<{w.d}>", "kernel_ms": round(ev_ms, 4)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -174,6 +231,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline sample budget (0 = skip)")
     ap.add_argument("--fixed-tiles", action="store_true",
                     help="plan with the fixed-tile baseline (one 128x128 tile per selected block pair, no packing)")
+    ap.add_argument("--chunk-select", action="store_true",
+                    help="time the chunk selection instead (default workload then 5: chunk-indexed GQA prefill)")
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward pass instead (default workload then 4: independent Q/K partitions)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -200,12 +259,18 @@ def main():
         return
 
     if args.workload is None:
-        args.workload = 4 if args.bwd else 3
+        args.workload = 4 if args.bwd else (5 if args.chunk_select else 3)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.perf_counter()
     w = make(args.workload)
     log(f"[bench] workload {w.name}: inputs generated in {time.perf_counter() - t0:.1f} s")
+
+    if args.chunk_select:
+        if args.workload != 5:
+            raise SystemExit("--chunk-select runs on workload 5 (chunk-indexed GQA prefill)")
+        bench_chunk_select(args, w, dev)
+        return
 
     t0 = time.perf_counter()
     plan = bs.Plan.from_workload(w, flags=bs.PLAN_FIXED_TILES if args.fixed_tiles else 0)

@@ -20,7 +20,8 @@ __all__ = [
     "BsattnError", "Problem", "Layout", "Selection", "Stats", "PlanView", "Plan", "library",
     "bsattn_plan_create", "bsattn_plan_create_ex", "PLAN_FIXED_TILES", "bsattn_plan_device_bytes", "bsattn_plan_upload", "bsattn_plan_stats",
     "bsattn_plan_export", "bsattn_plan_export_bwd", "PlanBwdView", "bsattn_fwd", "bsattn_fwd_shape",
-    "bsattn_bwd_workspace_bytes", "bsattn_bwd", "bsattn_plan_destroy", "bsattn_status_string", "bsattn_last_hip_error", "SHAPE_128x128", "SHAPE_64x256", "PAGE_SIZE",
+    "bsattn_bwd_workspace_bytes", "bsattn_bwd", "bsattn_chunk_select", "ChunkProblem", "chunk_select",
+    "bsattn_plan_destroy", "bsattn_status_string", "bsattn_last_hip_error", "SHAPE_128x128", "SHAPE_64x256", "PAGE_SIZE",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsattn.so")
@@ -74,6 +75,13 @@ class PlanView(ctypes.Structure):
                 ("pl_ptr", _i64p), ("pl_pages", _i32p)]
 
 
+class ChunkProblem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("Nq", ctypes.c_int32),
+                ("Nk", ctypes.c_int32), ("d", ctypes.c_int32), ("chunk", ctypes.c_int32), ("topk", ctypes.c_int32),
+                ("query_index", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3)]
+
+
 class PlanBwdView(ctypes.Structure):
     _fields_ = [("n_qpages", ctypes.c_int64), ("qpage_qblock", _i32p), ("qpage_slot0", _i32p),
                 ("qpage_nvalid", _i32p), ("n_dq_tiles", ctypes.c_int64), ("dqt_qblock", _i32p), ("dqt_row0", _i32p),
@@ -85,8 +93,8 @@ _lib: Optional[ctypes.CDLL] = None
 
 EXPORTED = ["bsattn_plan_create", "bsattn_plan_create_ex", "bsattn_plan_device_bytes", "bsattn_plan_upload", "bsattn_plan_stats",
             "bsattn_plan_export", "bsattn_plan_export_bwd", "bsattn_fwd", "bsattn_fwd_shape",
-            "bsattn_bwd_workspace_bytes", "bsattn_bwd", "bsattn_plan_destroy", "bsattn_status_string",
-            "bsattn_last_hip_error"]
+            "bsattn_bwd_workspace_bytes", "bsattn_bwd", "bsattn_chunk_select", "bsattn_plan_destroy",
+            "bsattn_status_string", "bsattn_last_hip_error"]
 
 
 def library() -> ctypes.CDLL:
@@ -112,6 +120,7 @@ def library() -> ctypes.CDLL:
     lib.bsattn_fwd_shape.argtypes = [vp, ctypes.c_int32, vp, vp, vp, vp, vp, ctypes.c_float, vp]
     lib.bsattn_bwd_workspace_bytes.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t)]
     lib.bsattn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, ctypes.c_size_t, vp]
+    lib.bsattn_chunk_select.argtypes = [ctypes.POINTER(ChunkProblem), vp, vp, vp, vp, vp]
     lib.bsattn_plan_destroy.argtypes = [vp]
     lib.bsattn_status_string.argtypes = [ctypes.c_int]
     lib.bsattn_status_string.restype = ctypes.c_char_p
@@ -234,6 +243,38 @@ def bsattn_bwd(plan, q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: in
     _check(library().bsattn_bwd(plan, vp(q_ptr), vp(k_ptr), vp(v_ptr), vp(o_ptr), vp(lse_ptr), vp(do_ptr),
                                 vp(dq_ptr), vp(dk_ptr), vp(dv_ptr), ctypes.c_float(scale), vp(ws_ptr), ws_bytes,
                                 vp(stream)), "bsattn_bwd")
+
+
+def bsattn_chunk_select(problem: ChunkProblem, q_ptr: int, k_ptr: int, summ_ptr: int, chunks_ptr: int,
+                        stream: int = 0) -> None:
+    vp = ctypes.c_void_p
+    _check(library().bsattn_chunk_select(ctypes.byref(problem), vp(q_ptr), vp(k_ptr), vp(summ_ptr), vp(chunks_ptr),
+                                         vp(stream)), "bsattn_chunk_select")
+
+
+def chunk_select(q, k, Hkv: int, chunk: int, topk: int, query_index: int = -1, stream=None):
+    """Chunk summaries and the top-k chunks per (batch, KV group) on the device.
+    q [B, Nq, Hq, d], k [B, Nk, Hkv, d] bf16 device tensors (d contiguous).  Returns
+    (summaries float32 [B, Hkv, n_chunks, d], chunks int32 [B, Hkv, topk] ascending)."""
+    import torch
+    B, Nq, Hq, d = q.shape
+    Nk = k.shape[1]
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or q.stride(3) != 1 or k.stride(3) != 1:
+        raise BsattnError(1, "chunk_select: q and k must be bf16 with d contiguous")
+    pr = ChunkProblem()
+    pr.B, pr.Hq, pr.Hkv, pr.Nq, pr.Nk, pr.d = B, Hq, Hkv, Nq, Nk, d
+    pr.chunk, pr.topk = chunk, topk
+    pr.query_index = query_index if query_index >= 0 else Nq + query_index
+    pr.reserved = 0
+    pr.q_stride[:] = tuple(q.stride()[:3])
+    pr.k_stride[:] = tuple(k.stride()[:3])
+    n = -(-Nk // chunk)
+    summ = torch.empty((B, Hkv, n, d), dtype=torch.float32, device=q.device)
+    chunks = torch.empty((B, Hkv, topk), dtype=torch.int32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    bsattn_chunk_select(pr, q.data_ptr(), k.data_ptr(), summ.data_ptr(), chunks.data_ptr(), stream)
+    return summ, chunks
 
 
 def bsattn_plan_destroy(plan) -> None:

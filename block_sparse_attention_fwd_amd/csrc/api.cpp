@@ -13,6 +13,7 @@
 namespace bsattn {
 hipError_t launch_fwd_shape(const FwdParams& p, int shape, int d, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, int d, hipStream_t stream);
+hipError_t launch_chunk_select(const ChunkParams& p, hipStream_t stream);
 }
 
 namespace {
@@ -263,6 +264,36 @@ int run_bwd(const bsattn_plan* plan, const void* q, const void* k, const void* v
 }  // namespace
 
 extern "C" {
+
+int bsattn_chunk_select(const bsattn_chunk_problem* pr, const void* q, const void* k, float* summaries,
+                        int32_t* chunks, void* stream) {
+  if (pr == nullptr || q == nullptr || k == nullptr || summaries == nullptr || chunks == nullptr) return BSATTN_E_ARG;
+  if (pr->B < 1 || pr->Hq < 1 || pr->Hkv < 1 || pr->Hq % pr->Hkv != 0 || pr->Nq < 1 || pr->Nk < 1 || pr->chunk < 1)
+    return BSATTN_E_ARG;
+  if (pr->query_index < 0 || pr->query_index >= pr->Nq) return BSATTN_E_ARG;
+  if (pr->d != 64 && pr->d != 128) return BSATTN_E_UNSUPPORTED;
+  const int64_t n = (int64_t(pr->Nk) + pr->chunk - 1) / pr->chunk;
+  if (pr->topk < 1 || pr->topk > n) return BSATTN_E_ARG;
+  if (n > 8192) return BSATTN_E_UNSUPPORTED;
+  for (const int64_t* st : {pr->q_stride, pr->k_stride})
+    if (st[0] < 0 || st[1] < 0 || st[2] < 0 || st[0] % 8 != 0 || st[1] % 8 != 0 || st[2] % 8 != 0) return BSATTN_E_ARG;
+  if ((reinterpret_cast<uintptr_t>(k) & 15) != 0 || (reinterpret_cast<uintptr_t>(summaries) & 15) != 0 ||
+      (reinterpret_cast<uintptr_t>(q) & 1) != 0 || (reinterpret_cast<uintptr_t>(chunks) & 3) != 0)
+    return BSATTN_E_ARG;
+  bsattn::ChunkParams cp{};
+  cp.q = q; cp.k = k; cp.summ = summaries; cp.chunks = chunks;
+  cp.q_sb = pr->q_stride[0]; cp.q_sn = pr->q_stride[1]; cp.q_sh = pr->q_stride[2];
+  cp.k_sb = pr->k_stride[0]; cp.k_sn = pr->k_stride[1]; cp.k_sh = pr->k_stride[2];
+  cp.B = pr->B; cp.Hq = pr->Hq; cp.Hkv = pr->Hkv; cp.Nq = pr->Nq; cp.Nk = pr->Nk; cp.d = pr->d;
+  cp.grp = pr->Hq / pr->Hkv;
+  cp.chunk = pr->chunk; cp.topk = pr->topk; cp.n_chunks = int32_t(n); cp.query_index = pr->query_index;
+  int32_t np2 = 1;
+  while (np2 < n) np2 <<= 1;
+  cp.n_pad = np2;
+  hipError_t e = bsattn::launch_chunk_select(cp, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return BSATTN_OK;
+}
 
 int bsattn_bwd_workspace_bytes(const bsattn_plan* plan, size_t* bytes) {
   if (plan == nullptr || bytes == nullptr) return BSATTN_E_ARG;

@@ -74,4 +74,16 @@ struct BwdParams {
   float scale, scale_log2;
 };
 
+// Chunk selection: summaries of key chunks and the top-k chunks per (batch, KV group).
+struct ChunkParams {
+  const void* q;
+  const void* k;
+  float* summ;      // [B, Hkv, n_chunks, d] float32
+  int32_t* chunks;  // [B, Hkv, topk], ascending chunk ids
+  int64_t q_sb, q_sn, q_sh;
+  int64_t k_sb, k_sn, k_sh;
+  int32_t B, Hq, Hkv, Nq, Nk, d, grp;
+  int32_t chunk, topk, n_chunks, n_pad, query_index;
+};
+
 }  // namespace bsattn

@@ -243,6 +243,37 @@ int bsattn_bwd(const bsattn_plan* plan, const void* q, const void* k, const void
                const float* lse, const void* dout, void* dq, void* dk, void* dv, float scale,
                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Chunk selection (CISA abstract, fugumt page 4, sentences 3-5: fixed-size KV chunks
+ * chosen with compact summaries of the keys, one indexing query per KV group, the selection
+ * shared by the group's queries).  Q [B, Nq, Hq, d] and K [B, Nk, Hkv, d] are bf16 with the
+ * given element strides (d contiguous, K rows 16-byte aligned).  Chunk c holds key tokens
+ * [c * chunk, min(Nk, (c + 1) * chunk)); n_chunks = ceil(Nk / chunk).  For each batch b and
+ * KV group g:
+ *     summary[b, g, c] = mean of the chunk's keys (float32)
+ *     iq[b, g]         = mean over the group's query heads of Q[b, query_index, h, :]
+ *     score            = <summary, iq>
+ * and the topk highest-scoring chunks (ties to the lower chunk id) are written to
+ * chunks[b, g, :] in ascending order.  In an attention problem they form the selection
+ * row of unit (b, g) (selection n_b = B, n_h = Hkv) for a Q block of the queries that share
+ * it.  summaries: caller-owned device float32 [B, Hkv, n_chunks, d], written (16-byte
+ * aligned); chunks: caller-owned device int32 [B, Hkv, topk], written.  Asynchronous on
+ * stream, two kernel launches, no allocation.  Errors: BSATTN_E_ARG for null or misaligned
+ * pointers, Hq not a multiple of Hkv, query_index outside [0, Nq) or topk outside
+ * [1, n_chunks]; BSATTN_E_UNSUPPORTED for d not 64/128 or n_chunks > 8192; BSATTN_E_HIP on
+ * a launch error. */
+typedef struct bsattn_chunk_problem {
+  int32_t B, Hq, Hkv, Nq, Nk, d;
+  int32_t chunk;        /* key tokens per chunk */
+  int32_t topk;         /* chunks kept per (batch, KV group) */
+  int32_t query_index;  /* the query row whose heads form the indexing query */
+  int32_t reserved;     /* 0 */
+  int64_t q_stride[3];
+  int64_t k_stride[3];
+} bsattn_chunk_problem;
+
+int bsattn_chunk_select(const bsattn_chunk_problem* problem, const void* q, const void* k, float* summaries,
+                        int32_t* chunks, void* stream);
+
 int bsattn_plan_destroy(bsattn_plan* plan);
 
 const char* bsattn_status_string(int status);

@@ -167,3 +167,23 @@ def test_library_exports_every_declared_symbol():
     for name in declared:
         assert name in syms, name
         assert hasattr(bs.library(), name)
+
+
+def test_chunk_select_argument_errors():
+    def st(**kw):
+        pr = bs.ChunkProblem()
+        base = dict(B=1, Hq=4, Hkv=2, Nq=8, Nk=640, d=128, chunk=64, topk=4, query_index=7, reserved=0)
+        base.update(kw)
+        for k, v in base.items():
+            setattr(pr, k, v)
+        pr.q_stride[:] = (8 * 4 * 128, 4 * 128, 128)
+        pr.k_stride[:] = (640 * 2 * 128, 2 * 128, 128)
+        return bs.library().bsattn_chunk_select(ctypes.byref(pr), ctypes.c_void_p(256), ctypes.c_void_p(256),
+                                                ctypes.c_void_p(256), ctypes.c_void_p(256), None)
+    assert st(topk=11) == 1               # more than ceil(640 / 64) = 10 chunks
+    assert st(topk=0) == 1
+    assert st(query_index=8) == 1
+    assert st(Hq=3) == 1
+    assert st(d=96) == 4
+    assert st(Nk=64 * 8193, topk=4) == 4  # more than 8192 chunks
+    assert bs.library().bsattn_chunk_select(None, None, None, None, None, None) == 1
