@@ -229,6 +229,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=None, help="benchmark workload 1-5 (default 3: video-DiT 3D)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU-baseline sample budget (0 = skip)")
+    ap.add_argument("--natural-order", action="store_true",
+                    help="dispatch Q tiles in Q-block order, ignoring the workload's locality hint")
     ap.add_argument("--fixed-tiles", action="store_true",
                     help="plan with the fixed-tile baseline (one 128x128 tile per selected block pair, no packing)")
     ap.add_argument("--chunk-select", action="store_true",
@@ -273,7 +275,8 @@ def main():
         return
 
     t0 = time.perf_counter()
-    plan = bs.Plan.from_workload(w, flags=bs.PLAN_FIXED_TILES if args.fixed_tiles else 0)
+    plan = bs.Plan.from_workload(w, block_order=not args.natural_order,
+                                 flags=bs.PLAN_FIXED_TILES if args.fixed_tiles else 0)
     t_plan = time.perf_counter() - t0
     st = plan.stats
     plan.upload()
@@ -351,6 +354,8 @@ def main():
                    "kernel_ms": {"128x128": round(k128, 4), "64x256": round(k64, 4)},
                    "plan": "fixed 128x128 tiles per selected block pair (no packing)" if args.fixed_tiles
                    else "packed pages, routed Q tiles",
+                   "dispatch_order": "Q blocks in order" if (args.natural_order or w.q_block_order is None)
+                   else "workload hint (cubes by h, t, w)",
                    "plan_ms": round(t_plan * 1e3, 2)},
         "roofline": roofline,
         "cpu_baseline": cpu,

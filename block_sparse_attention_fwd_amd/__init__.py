@@ -18,7 +18,7 @@ import numpy as np
 
 __all__ = [
     "BsattnError", "Problem", "Layout", "Selection", "Stats", "PlanView", "Plan", "library",
-    "bsattn_plan_create", "bsattn_plan_create_ex", "PLAN_FIXED_TILES", "bsattn_plan_device_bytes", "bsattn_plan_upload", "bsattn_plan_stats",
+    "bsattn_plan_create", "bsattn_plan_create_ex", "bsattn_plan_set_block_order", "PLAN_FIXED_TILES", "bsattn_plan_device_bytes", "bsattn_plan_upload", "bsattn_plan_stats",
     "bsattn_plan_export", "bsattn_plan_export_bwd", "PlanBwdView", "bsattn_fwd", "bsattn_fwd_shape",
     "bsattn_bwd_workspace_bytes", "bsattn_bwd", "bsattn_chunk_select", "ChunkProblem", "chunk_select",
     "bsattn_plan_destroy", "bsattn_status_string", "bsattn_last_hip_error", "SHAPE_128x128", "SHAPE_64x256", "PAGE_SIZE",
@@ -91,7 +91,7 @@ class PlanBwdView(ctypes.Structure):
 
 _lib: Optional[ctypes.CDLL] = None
 
-EXPORTED = ["bsattn_plan_create", "bsattn_plan_create_ex", "bsattn_plan_device_bytes", "bsattn_plan_upload", "bsattn_plan_stats",
+EXPORTED = ["bsattn_plan_create", "bsattn_plan_create_ex", "bsattn_plan_set_block_order", "bsattn_plan_device_bytes", "bsattn_plan_upload", "bsattn_plan_stats",
             "bsattn_plan_export", "bsattn_plan_export_bwd", "bsattn_fwd", "bsattn_fwd_shape",
             "bsattn_bwd_workspace_bytes", "bsattn_bwd", "bsattn_chunk_select", "bsattn_plan_destroy",
             "bsattn_status_string", "bsattn_last_hip_error"]
@@ -111,6 +111,7 @@ def library() -> ctypes.CDLL:
     lib.bsattn_plan_create_ex.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(Layout), ctypes.POINTER(Layout),
                                           ctypes.POINTER(Selection), ctypes.c_int32, ctypes.c_int32,
                                           ctypes.POINTER(vp)]
+    lib.bsattn_plan_set_block_order.argtypes = [vp, _i32p, ctypes.c_int32]
     lib.bsattn_plan_device_bytes.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t)]
     lib.bsattn_plan_upload.argtypes = [vp, vp, ctypes.c_size_t, vp]
     lib.bsattn_plan_stats.argtypes = [vp, ctypes.POINTER(Stats)]
@@ -155,6 +156,12 @@ def bsattn_plan_create_ex(problem: Problem, q_layout: Layout, k_layout: Layout, 
                                            ctypes.byref(selection), page_size, flags, ctypes.byref(h)),
            "bsattn_plan_create_ex")
     return h
+
+
+def bsattn_plan_set_block_order(plan, order) -> None:
+    o = np.ascontiguousarray(order, dtype=np.int32)
+    _check(library().bsattn_plan_set_block_order(plan, o.ctypes.data_as(_i32p), int(o.shape[0])),
+           "bsattn_plan_set_block_order")
 
 
 def bsattn_plan_device_bytes(plan) -> int:
@@ -334,9 +341,15 @@ class Plan:
         self.device_buffer = None
 
     @classmethod
-    def from_workload(cls, w, **kw):
-        return cls(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.q_offsets, w.q_perm, w.k_offsets, w.k_perm, w.sel_nb,
-                   w.sel_nh, w.sel_row_ptr, w.sel_kblk, causal=w.causal, q_pos0=w.q_pos0, **kw)
+    def from_workload(cls, w, block_order=True, **kw):
+        """A plan for a workload object; its Q-block dispatch hint (``q_block_order``) is
+        applied unless ``block_order`` is False."""
+        p = cls(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.q_offsets, w.q_perm, w.k_offsets, w.k_perm, w.sel_nb,
+                w.sel_nh, w.sel_row_ptr, w.sel_kblk, causal=w.causal, q_pos0=w.q_pos0, **kw)
+        order = getattr(w, "q_block_order", None)
+        if block_order and order is not None:
+            p.set_block_order(order)
+        return p
 
     def __del__(self):
         h = getattr(self, "handle", None)
@@ -353,6 +366,11 @@ class Plan:
 
     def export_bwd(self) -> dict:
         return bsattn_plan_export_bwd(self.handle)
+
+    def set_block_order(self, order):
+        """Dispatch order of the Q blocks (a locality hint; upload afterwards)."""
+        bsattn_plan_set_block_order(self.handle, order)
+        return self
 
     @property
     def device_bytes(self) -> int:

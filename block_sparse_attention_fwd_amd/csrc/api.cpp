@@ -59,6 +59,15 @@ int bsattn_plan_create(const bsattn_problem* problem, const bsattn_layout* q_lay
   return bsattn_plan_create_ex(problem, q_layout, k_layout, selection, page_size, 0, out);
 }
 
+int bsattn_plan_set_block_order(bsattn_plan* plan, const int32_t* order, int32_t n_qblocks) {
+  if (plan == nullptr) return BSATTN_E_ARG;
+  try {
+    return bsattn::set_block_order(plan, order, n_qblocks);
+  } catch (const std::bad_alloc&) {
+    return BSATTN_E_OOM;
+  }
+}
+
 int bsattn_plan_device_bytes(const bsattn_plan* plan, size_t* bytes) {
   if (plan == nullptr || bytes == nullptr) return BSATTN_E_ARG;
   *bytes = plan->image.size();

@@ -45,6 +45,37 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
 
+void write_qtiles(bsattn_plan* p) {
+  // dispatch order: Q blocks in p->qblock_order (ascending when empty), each block's tiles in
+  // row order; the canonical (exported) tile arrays keep Q-block order
+  std::vector<int32_t> rank(size_t(p->nqb));
+  for (int32_t i = 0; i < p->nqb; ++i) rank[size_t(i)] = i;
+  if (!p->qblock_order.empty())
+    for (int32_t i = 0; i < p->nqb; ++i) rank[size_t(p->qblock_order[size_t(i)])] = i;
+  for (int sh = 0; sh < kShapes; ++sh) {
+    std::vector<size_t> ord;
+    for (size_t t = 0; t < p->qt_shape.size(); ++t)
+      if (p->qt_shape[t] == sh) ord.push_back(t);
+    std::stable_sort(ord.begin(), ord.end(),
+                     [&](size_t a, size_t b) { return rank[size_t(p->qt_qblock[a])] < rank[size_t(p->qt_qblock[b])]; });
+    QTileDev* q = reinterpret_cast<QTileDev*>(p->image.data() + p->off_qt[sh]);
+    int32_t i = 0;
+    for (size_t t : ord) q[i++] = QTileDev{p->qt_row0[t], p->qt_rows[t], p->qt_qblock[t], 0};
+  }
+}
+
+int set_block_order(bsattn_plan* p, const int32_t* order, int32_t n) {
+  if (n != p->nqb || (n > 0 && order == nullptr)) return BSATTN_E_ARG;
+  std::vector<uint8_t> seen(size_t(n), 0);
+  for (int32_t i = 0; i < n; ++i) {
+    if (order[i] < 0 || order[i] >= n || seen[size_t(order[i])]) return BSATTN_E_ARG;
+    seen[size_t(order[i])] = 1;
+  }
+  p->qblock_order.assign(order, order + n);
+  write_qtiles(p);
+  return BSATTN_OK;
+}
+
 int build_plan(const bsattn_problem& prob, const bsattn_layout& ql, const bsattn_layout& kl,
                const bsattn_selection& sel, int32_t flags, bsattn_plan* p) {
   if ((flags & ~int32_t(BSATTN_PLAN_FIXED_TILES)) != 0) return BSATTN_E_ARG;
@@ -279,14 +310,7 @@ int build_plan(const bsattn_problem& prob, const bsattn_layout& ql, const bsattn
   p->image.assign(std::max<size_t>(off, 256), 0);
 
   uint8_t* img = p->image.data();
-  for (int sh = 0; sh < kShapes; ++sh) {
-    QTileDev* q = reinterpret_cast<QTileDev*>(img + p->off_qt[sh]);
-    int32_t i = 0;
-    for (size_t t = 0; t < p->qt_shape.size(); ++t) {
-      if (p->qt_shape[t] != sh) continue;
-      q[i++] = QTileDev{p->qt_row0[t], p->qt_rows[t], p->qt_qblock[t], 0};
-    }
-  }
+  write_qtiles(p);
   int32_t* plp = reinterpret_cast<int32_t*>(img + p->off_plptr);
   for (size_t r = 0; r <= size_t(n_rows); ++r) plp[r] = int32_t(p->pl_ptr[r]);
   int32_t* ent = reinterpret_cast<int32_t*>(img + p->off_plent);

@@ -38,6 +38,7 @@ constexpr int kBwdTileRows = 64;
 struct bsattn_plan {
   bsattn_problem prob{};
   int32_t flags = 0;  // BSATTN_PLAN_*
+  std::vector<int32_t> qblock_order;  // dispatch order of Q blocks (empty: ascending)
   int32_t nqb = 0, nkb = 0, sel_nb = 1, sel_nh = 1, n_units = 1;
   // canonical arrays (exported)
   std::vector<int32_t> page_kblock, page_slot0, page_nvalid;
@@ -68,4 +69,8 @@ namespace bsattn {
 // flags: BSATTN_PLAN_* (0 = the packed plan)
 int build_plan(const bsattn_problem& prob, const bsattn_layout& ql, const bsattn_layout& kl,
                const bsattn_selection& sel, int32_t flags, bsattn_plan* p);
+// Writes the forward Q-tile tables of the device image in dispatch order.
+void write_qtiles(bsattn_plan* p);
+// Validates a permutation of the Q blocks and makes it the dispatch order.
+int set_block_order(bsattn_plan* p, const int32_t* order, int32_t n);
 }  // namespace bsattn

@@ -179,6 +179,14 @@ int bsattn_plan_create_ex(const bsattn_problem* problem, const bsattn_layout* q_
                           const bsattn_layout* k_layout, const bsattn_selection* selection,
                           int32_t page_size, int32_t flags, bsattn_plan** out);
 
+/* Dispatch order of the forward's Q tiles: order[i] is the i-th Q block whose tiles are
+ * launched (a permutation of [0, n_qblocks); each block's tiles stay in row order).  A
+ * locality hint only -- results do not change: Q tiles that run at the same time on one XCD
+ * and walk overlapping page lists at similar offsets share that XCD's L2.  The default is
+ * ascending block order.  It takes effect at the next bsattn_plan_upload.  Errors:
+ * BSATTN_E_ARG if order is not such a permutation. */
+int bsattn_plan_set_block_order(bsattn_plan* plan, const int32_t* order, int32_t n_qblocks);
+
 /* Bytes of device memory the plan needs (a multiple of 256). */
 int bsattn_plan_device_bytes(const bsattn_plan* plan, size_t* bytes);
 

@@ -130,6 +130,16 @@ def test_fixed_tiles_plan_same_results(case):
     check_rows(np.transpose(O, (0, 2, 1, 3)), L, np.transpose(Or, (0, 2, 1, 3)), Lr, f"fixed-{case}")
 
 
+def test_block_order_hint_same_bits():
+    # the dispatch order of Q blocks is a locality hint: every tile computes the same bits
+    w = make_random(**RANDOM_CASES[2])
+    a = bs.Plan.from_workload(w).upload()
+    b = bs.Plan.from_workload(w).set_block_order(np.random.default_rng(9).permutation(w.n_qblocks)).upload()
+    Oa, La, _ = run_gpu(w, plan=a)
+    Ob, Lb, _ = run_gpu(w, plan=b)
+    assert np.array_equal(Oa, Ob) and np.array_equal(La, Lb, equal_nan=True)
+
+
 def test_empty_rows_and_empty_selection():
     # no Q block selects anything: every row has no key
     w = make_random(111, B=1, Hq=2, Hkv=2, Nq=200, Nk=300, d=128, max_qblock=90, max_kblock=50, sel_mode="head")

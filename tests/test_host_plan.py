@@ -187,3 +187,17 @@ def test_chunk_select_argument_errors():
     assert st(d=96) == 4
     assert st(Nk=64 * 8193, topk=4) == 4  # more than 8192 chunks
     assert bs.library().bsattn_chunk_select(None, None, None, None, None, None) == 1
+
+
+def test_block_order_hint_validates_and_keeps_canonical_arrays():
+    w = make(3, with_tensors=False)
+    a = bs.Plan.from_workload(w, block_order=False)
+    b = bs.Plan.from_workload(w)  # the cube workload's (h, t, w) hint
+    for k, v in a.export().items():
+        assert np.array_equal(v, b.export()[k]), k
+    assert a.stats["physical"] == b.stats["physical"]
+    assert sorted(w.q_block_order.tolist()) == list(range(w.n_qblocks))
+    with pytest.raises(bs.BsattnError):
+        a.set_block_order(np.zeros(w.n_qblocks, np.int32))        # not a permutation
+    with pytest.raises(bs.BsattnError):
+        a.set_block_order(np.arange(w.n_qblocks - 1, dtype=np.int32))  # wrong length
