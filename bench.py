@@ -360,8 +360,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
-    if args.fixed_tiles:
-        roofline["traffic"] = None  # the counter runs cover the packed plan only
+    if args.fixed_tiles or args.natural_order:
+        roofline["traffic"] = None  # the counter runs cover the default plan and order only
     print(json.dumps(out), flush=True)
 
 
