@@ -21,6 +21,7 @@ __all__ = [
     "bsattn_plan_create", "bsattn_plan_create_ex", "bsattn_plan_set_block_order", "PLAN_FIXED_TILES", "bsattn_plan_device_bytes", "bsattn_plan_upload", "bsattn_plan_stats",
     "bsattn_plan_export", "bsattn_plan_export_bwd", "PlanBwdView", "bsattn_fwd", "bsattn_fwd_shape",
     "bsattn_bwd_workspace_bytes", "bsattn_bwd", "bsattn_chunk_select", "ChunkProblem", "chunk_select",
+    "bsattn_decode_workspace_bytes", "bsattn_fwd_decode",
     "bsattn_plan_destroy", "bsattn_status_string", "bsattn_last_hip_error", "SHAPE_128x128", "SHAPE_64x256", "PAGE_SIZE",
 ]
 
@@ -93,8 +94,8 @@ _lib: Optional[ctypes.CDLL] = None
 
 EXPORTED = ["bsattn_plan_create", "bsattn_plan_create_ex", "bsattn_plan_set_block_order", "bsattn_plan_device_bytes", "bsattn_plan_upload", "bsattn_plan_stats",
             "bsattn_plan_export", "bsattn_plan_export_bwd", "bsattn_fwd", "bsattn_fwd_shape",
-            "bsattn_bwd_workspace_bytes", "bsattn_bwd", "bsattn_chunk_select", "bsattn_plan_destroy",
-            "bsattn_status_string", "bsattn_last_hip_error"]
+            "bsattn_bwd_workspace_bytes", "bsattn_bwd", "bsattn_chunk_select", "bsattn_decode_workspace_bytes",
+            "bsattn_fwd_decode", "bsattn_plan_destroy", "bsattn_status_string", "bsattn_last_hip_error"]
 
 
 def library() -> ctypes.CDLL:
@@ -121,6 +122,8 @@ def library() -> ctypes.CDLL:
     lib.bsattn_fwd_shape.argtypes = [vp, ctypes.c_int32, vp, vp, vp, vp, vp, ctypes.c_float, vp]
     lib.bsattn_bwd_workspace_bytes.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t)]
     lib.bsattn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, ctypes.c_size_t, vp]
+    lib.bsattn_decode_workspace_bytes.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t)]
+    lib.bsattn_fwd_decode.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, ctypes.c_size_t, vp]
     lib.bsattn_chunk_select.argtypes = [ctypes.POINTER(ChunkProblem), vp, vp, vp, vp, vp]
     lib.bsattn_plan_destroy.argtypes = [vp]
     lib.bsattn_status_string.argtypes = [ctypes.c_int]
@@ -250,6 +253,19 @@ def bsattn_bwd(plan, q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: in
     _check(library().bsattn_bwd(plan, vp(q_ptr), vp(k_ptr), vp(v_ptr), vp(o_ptr), vp(lse_ptr), vp(do_ptr),
                                 vp(dq_ptr), vp(dk_ptr), vp(dv_ptr), ctypes.c_float(scale), vp(ws_ptr), ws_bytes,
                                 vp(stream)), "bsattn_bwd")
+
+
+def bsattn_decode_workspace_bytes(plan) -> int:
+    n = ctypes.c_size_t()
+    _check(library().bsattn_decode_workspace_bytes(plan, ctypes.byref(n)), "bsattn_decode_workspace_bytes")
+    return int(n.value)
+
+
+def bsattn_fwd_decode(plan, q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, scale: float, ws_ptr: int,
+                      ws_bytes: int, stream: int = 0) -> None:
+    vp = ctypes.c_void_p
+    _check(library().bsattn_fwd_decode(plan, vp(q_ptr), vp(k_ptr), vp(v_ptr), vp(o_ptr), vp(lse_ptr),
+                                       ctypes.c_float(scale), vp(ws_ptr), ws_bytes, vp(stream)), "bsattn_fwd_decode")
 
 
 def bsattn_chunk_select(problem: ChunkProblem, q_ptr: int, k_ptr: int, summ_ptr: int, chunks_ptr: int,
@@ -446,3 +462,29 @@ class Plan:
                    do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), scale, workspace.data_ptr(),
                    workspace.numel() * workspace.element_size(), stream)
         return dq, dk, dv
+
+    def fwd_decode(self, q, k, v, o=None, lse=None, workspace=None, scale=None, stream=None):
+        """The forward for small query blocks with the query heads of a KV group stacked
+        (bsattn_fwd_decode); same outputs as ``fwd``."""
+        import torch
+        pr = self.problem
+        if o is None:
+            o = torch.empty((pr.B, pr.Nq, pr.Hq, pr.d), dtype=torch.bfloat16, device=q.device)
+        if lse is None:
+            lse = torch.empty((pr.B, pr.Hq, pr.Nq), dtype=torch.float32, device=q.device)
+        for name, t, st in (("q", q, pr.q_stride), ("k", k, pr.k_stride), ("v", v, pr.v_stride),
+                            ("o", o, pr.o_stride)):
+            if t.dtype != torch.bfloat16 or not t.is_cuda:
+                raise BsattnError(1, f"bsattn_fwd_decode: {name} must be a bf16 device tensor")
+            if tuple(t.stride()[:3]) != tuple(st) or t.stride(3) != 1:
+                raise BsattnError(1, f"bsattn_fwd_decode: {name} strides {t.stride()} differ from the plan's")
+        nws = bsattn_decode_workspace_bytes(self.handle)
+        if workspace is None:
+            workspace = torch.empty(nws, dtype=torch.uint8, device=q.device)
+        if scale is None:
+            scale = 1.0 / float(pr.d) ** 0.5
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        bsattn_fwd_decode(self.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), scale,
+                          workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
+        return o, lse

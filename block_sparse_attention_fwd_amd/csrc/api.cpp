@@ -14,6 +14,7 @@ namespace bsattn {
 hipError_t launch_fwd_shape(const FwdParams& p, int shape, int d, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, int d, hipStream_t stream);
 hipError_t launch_chunk_select(const ChunkParams& p, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t stream);
 }
 
 namespace {
@@ -273,6 +274,101 @@ int run_bwd(const bsattn_plan* plan, const void* q, const void* k, const void* v
 }  // namespace
 
 extern "C" {
+
+namespace {
+// Split of the decode work: every Q block fits one stacked tile (n * group <= 32, so every
+// tile is a 64-row tile), the query heads of a group share a selection unit, and each page
+// list is cut into n_splits ranges of pps pages (a multiple of 8) so that about 2048
+// workgroups run.  Returns BSATTN_OK or BSATTN_E_UNSUPPORTED.
+int decode_geometry(const bsattn_plan* plan, int32_t* n_splits, int32_t* pps, size_t* ws_bytes) {
+  const bsattn_problem& pr = plan->prob;
+  const int32_t grp = pr.Hq / pr.Hkv;
+  if (plan->flags != 0 || plan->n_qt[0] != 0) return BSATTN_E_UNSUPPORTED;
+  if (plan->sel_nh == pr.Hq && grp > 1) return BSATTN_E_UNSUPPORTED;
+  int32_t max_rows = 0;
+  for (size_t t = 0; t < plan->qt_rows.size(); ++t) max_rows = std::max(max_rows, plan->qt_rows[t]);
+  if (int64_t(max_rows) * grp > 32) return BSATTN_E_UNSUPPORTED;
+  int64_t max_list = 0;
+  for (size_t r = 0; r + 1 < plan->pl_ptr.size(); ++r) max_list = std::max(max_list, plan->pl_ptr[r + 1] - plan->pl_ptr[r]);
+  const int64_t items = int64_t(pr.B) * pr.Hkv * plan->n_qt[1];
+  int64_t ns = items > 0 ? (2048 + items - 1) / items : 1;
+  ns = std::max<int64_t>(1, std::min<int64_t>(ns, (max_list + 7) / 8));
+  int64_t per = (max_list + ns - 1) / ns;
+  per = std::max<int64_t>(8, (per + 7) / 8 * 8);
+  ns = std::max<int64_t>(1, (max_list + per - 1) / per);
+  if (items * ns >= (int64_t(1) << 31) || per >= (int64_t(1) << 30)) return BSATTN_E_UNSUPPORTED;
+  *n_splits = int32_t(ns);
+  *pps = int32_t(per);
+  *ws_bytes = std::max<size_t>(256, size_t(items * ns) * 32 * size_t(pr.d + 2) * sizeof(float));
+  return BSATTN_OK;
+}
+}  // namespace
+
+int bsattn_decode_workspace_bytes(const bsattn_plan* plan, size_t* bytes) {
+  if (plan == nullptr || bytes == nullptr) return BSATTN_E_ARG;
+  int32_t ns, per;
+  return decode_geometry(plan, &ns, &per, bytes);
+}
+
+int bsattn_fwd_decode(const bsattn_plan* plan, const void* q, const void* k, const void* v, void* o, float* lse,
+                      float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (plan == nullptr) return BSATTN_E_ARG;
+  if (plan->dev == nullptr) return BSATTN_E_STATE;
+  const bsattn_problem& pr = plan->prob;
+  int32_t ns = 0, per = 0;
+  size_t need = 0;
+  const int st = decode_geometry(plan, &ns, &per, &need);
+  if (st != BSATTN_OK) return st;
+  if (pr.Nq == 0) return BSATTN_OK;
+  if (q == nullptr || o == nullptr || lse == nullptr || workspace == nullptr || workspace_bytes < need) return BSATTN_E_ARG;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0) return BSATTN_E_ARG;
+  if (pr.Nk > 0 && (k == nullptr || v == nullptr)) return BSATTN_E_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return BSATTN_E_ARG;
+  auto aligned = [](const void* ptr, const int64_t* sd) {
+    return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0 && sd[0] % 8 == 0 && sd[1] % 8 == 0 && sd[2] % 8 == 0 &&
+           sd[0] >= 0 && sd[1] >= 0 && sd[2] >= 0;
+  };
+  if (!aligned(q, pr.q_stride) || !aligned(o, pr.o_stride)) return BSATTN_E_ARG;
+  if (pr.Nk > 0 && (!aligned(k, pr.k_stride) || !aligned(v, pr.v_stride))) return BSATTN_E_ARG;
+  const int64_t k_extent = pr.Nk > 0 ? (int64_t(pr.Nk) - 1) * pr.k_stride[1] * 2 + pr.d * 2 : 0;
+  const int64_t v_extent = pr.Nk > 0 ? (int64_t(pr.Nk) - 1) * pr.v_stride[1] * 2 + pr.d * 2 : 0;
+  if (k_extent > 0xffffffffLL || v_extent > 0xffffffffLL) return BSATTN_E_UNSUPPORTED;
+  const uint8_t* base = static_cast<const uint8_t*>(plan->dev);
+  bsattn::DecodeParams dp{};
+  dp.q = q; dp.k = k; dp.v = v; dp.o = o; dp.lse = lse;
+  dp.q_sb = pr.q_stride[0]; dp.q_sn = pr.q_stride[1]; dp.q_sh = pr.q_stride[2];
+  dp.k_sb = pr.k_stride[0]; dp.k_sn = pr.k_stride[1]; dp.k_sh = pr.k_stride[2];
+  dp.v_sb = pr.v_stride[0]; dp.v_sn = pr.v_stride[1]; dp.v_sh = pr.v_stride[2];
+  dp.o_sb = pr.o_stride[0]; dp.o_sn = pr.o_stride[1]; dp.o_sh = pr.o_stride[2];
+  dp.qtiles = reinterpret_cast<const bsattn::QTileDev*>(base + plan->off_qt[1]);
+  dp.pl_ptr = reinterpret_cast<const int32_t*>(base + plan->off_plptr);
+  dp.pl_ent = reinterpret_cast<const int32_t*>(base + plan->off_plent);
+  dp.qperm = plan->has_qperm ? reinterpret_cast<const int32_t*>(base + plan->off_qperm) : nullptr;
+  dp.kperm = plan->has_kperm ? reinterpret_cast<const int32_t*>(base + plan->off_kperm) : nullptr;
+  dp.opart = static_cast<float*>(workspace);
+  const int64_t items = int64_t(pr.B) * pr.Hkv * plan->n_qt[1];
+  dp.mlpart = dp.opart + size_t(items * ns) * 32 * size_t(pr.d);
+  dp.q_pos0 = pr.q_pos0;
+  dp.k_extent = uint32_t(k_extent);
+  dp.v_extent = uint32_t(v_extent);
+  dp.k_sn_bytes = uint32_t(pr.k_stride[1] * 2);
+  dp.v_sn_bytes = uint32_t(pr.v_stride[1] * 2);
+  dp.n_qtiles = plan->n_qt[1];
+  dp.n_splits = ns;
+  dp.pps = per;
+  dp.B = pr.B; dp.Hq = pr.Hq; dp.Hkv = pr.Hkv; dp.Nq = pr.Nq; dp.Nk = pr.Nk;
+  dp.grp = pr.Hq / pr.Hkv;
+  dp.nqb = plan->nqb;
+  dp.sel_nh = plan->sel_nh;
+  dp.ub_mul = (plan->sel_nb == pr.B) ? 1 : 0;
+  dp.uh_div = (plan->sel_nh == pr.Hq) ? 1 : (plan->sel_nh == pr.Hkv ? dp.grp : pr.Hq);
+  dp.causal = pr.causal;
+  dp.scale = scale;
+  dp.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = bsattn::launch_decode(dp, pr.d, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return BSATTN_OK;
+}
 
 int bsattn_chunk_select(const bsattn_chunk_problem* pr, const void* q, const void* k, float* summaries,
                         int32_t* chunks, void* stream) {

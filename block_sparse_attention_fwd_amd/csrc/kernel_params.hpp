@@ -74,6 +74,34 @@ struct BwdParams {
   float scale, scale_log2;
 };
 
+// Decode / small query blocks: the query heads of a KV group stacked into one 32-column
+// tile per Q block, pages split over workgroups, partial softmax states merged after.
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t q_sb, q_sn, q_sh;
+  int64_t k_sb, k_sn, k_sh;
+  int64_t v_sb, v_sn, v_sh;
+  int64_t o_sb, o_sn, o_sh;
+  const QTileDev* qtiles;  // one tile per Q block (every block has at most 32 / grp rows)
+  const int32_t* pl_ptr;
+  const int32_t* pl_ent;
+  const int32_t* qperm;
+  const int32_t* kperm;
+  float* opart;   // workspace: [work][32][d] unnormalised O of a split
+  float* mlpart;  // workspace: [work][32][2] running max (log2 units) and sum of a split
+  int64_t q_pos0;
+  uint32_t k_extent, v_extent, k_sn_bytes, v_sn_bytes;
+  int32_t n_qtiles, n_splits, pps;  // tiles, splits per (b, g, tile), pages per split (multiple of 8)
+  int32_t B, Hq, Hkv, Nq, Nk, grp;
+  int32_t nqb, sel_nh, ub_mul, uh_div;
+  int32_t causal;
+  float scale, scale_log2;
+};
+
 // Chunk selection: summaries of key chunks and the top-k chunks per (batch, KV group).
 struct ChunkParams {
   const void* q;

@@ -251,6 +251,21 @@ int bsattn_bwd(const bsattn_plan* plan, const void* q, const void* k, const void
                const float* lse, const void* dout, void* dq, void* dk, void* dv, float scale,
                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Decode and other small query blocks (the same operation as bsattn_fwd).  When every Q
+ * block has at most 32 / (Hq / Hkv) rows and the query heads of a KV group share their
+ * selection unit (selection n_h = 1 or Hkv), the group's heads are stacked into the 32
+ * columns of one tile per Q block, so each selected K/V page is read once per group instead
+ * of once per head (CISA abstract, fugumt page 4, sentences 4-5: one indexing query per KV
+ * group, selections shared by the group's queries).  Each page list is split over many
+ * workgroups and the partial softmax states are merged exactly.  Same arguments as
+ * bsattn_fwd plus a caller-owned device workspace of at least bsattn_decode_workspace_bytes
+ * bytes (16-byte aligned; it holds the partial states).  Two launches, no allocation.
+ * BSATTN_E_UNSUPPORTED when the plan does not meet the conditions above (or was made with
+ * flags); other errors as for bsattn_fwd. */
+int bsattn_decode_workspace_bytes(const bsattn_plan* plan, size_t* bytes);
+int bsattn_fwd_decode(const bsattn_plan* plan, const void* q, const void* k, const void* v, void* o,
+                      float* lse, float scale, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Chunk selection (CISA abstract, fugumt page 4, sentences 3-5: fixed-size KV chunks
  * chosen with compact summaries of the keys, one indexing query per KV group, the selection
  * shared by the group's queries).  Q [B, Nq, Hq, d] and K [B, Nk, Hkv, d] are bf16 with the

@@ -201,3 +201,19 @@ def test_block_order_hint_validates_and_keeps_canonical_arrays():
         a.set_block_order(np.zeros(w.n_qblocks, np.int32))        # not a permutation
     with pytest.raises(bs.BsattnError):
         a.set_block_order(np.arange(w.n_qblocks - 1, dtype=np.int32))  # wrong length
+
+
+def test_decode_geometry_and_unsupported_plans():
+    w = make_chunk_gqa("decode", 7, B=2, Hq=16, Hkv=2, d=128, Nk=64 * 150, Nq=1, chunk=64, topk=40)
+    p = bs.Plan.from_workload(w)
+    assert bs.bsattn_decode_workspace_bytes(p.handle) > 0
+    big = make_random(8, B=1, Hq=8, Hkv=1, Nq=100, Nk=100, d=64, max_qblock=20, sel_mode="kv", with_tensors=False)
+    pb = bs.Plan.from_workload(big)  # Q blocks of up to 20 rows x 8 heads > 32 columns
+    with pytest.raises(bs.BsattnError) as e:
+        bs.bsattn_decode_workspace_bytes(pb.handle)
+    assert e.value.status == 4
+    per_head = make_random(9, B=1, Hq=4, Hkv=2, Nq=20, Nk=100, d=64, max_qblock=4, sel_mode="head",
+                           with_tensors=False)
+    with pytest.raises(bs.BsattnError) as e:
+        bs.bsattn_decode_workspace_bytes(bs.Plan.from_workload(per_head).handle)
+    assert e.value.status == 4
