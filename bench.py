@@ -12,7 +12,9 @@ cubes 2x8x8, 40 heads, d = 128, sliding-tile window +-1 t, +-2 h, +-2 w in cube 
 
 With ``--fixed-tiles`` the plan is the fixed-tile baseline (one 128x128 tile per selected
 block pair, no page packing, no 64x256 routing) -- the ablation of packing on the same
-kernels.  With ``--chunk-select`` a step is one ``bsattn_chunk_select`` call (chunk
+kernels.  With ``--decode`` a step is one ``bsattn_fwd_decode`` call (one query per
+sequence, the query heads of a KV group stacked; HBM-bound, GB/s), with the plain forward
+over the same plan timed beside it.  With ``--chunk-select`` a step is one ``bsattn_chunk_select`` call (chunk
 summaries and top-k chunks of the chunk-indexed prefill workload; HBM-bound, reported in
 GB/s).  With ``--bwd`` a step is one ``bsattn_bwd`` call (D = rowsum(dO * O), then the dK/dV and dQ
 kernels) on the independent Q/K partition workload, counted as 10 * d per useful pair.
@@ -222,6 +224,69 @@ def bench_chunk_select(args, w, dev):
     print(json.dumps(out), flush=True)
 
 
+def bench_decode(args, dev):
+    """One step = one bsattn_fwd_decode call: one decode query per sequence over the
+    chunk-indexed long context (4 x 262,144 keys, 8 KV groups of 8 query heads, top-2048
+    chunks of 64), the group's heads stacked.  HBM-bound: the selected K/V rows are read
+    once per KV group.  The plain forward over the same plan is timed beside it."""
+    import torch
+    import block_sparse_attention_fwd_amd as bs
+    from workloads.configs import make_chunk_gqa
+
+    t0 = time.perf_counter()
+    w = make_chunk_gqa("chunk-gqa-decode-b4-h64kv8-262144-d128", 5, B=4, Hq=64, Hkv=8, d=128, Nk=262144, Nq=1,
+                       chunk=64, topk=2048)
+    log(f"[bench] decode workload generated in {time.perf_counter() - t0:.1f} s")
+    plan = bs.Plan.from_workload(w).upload()
+    st = plan.stats
+
+    def to_dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = to_dev(w.q), to_dev(w.k), to_dev(w.v)
+    o = torch.empty((w.B, w.Nq, w.Hq, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
+    nws = bs.bsattn_decode_workspace_bytes(plan.handle)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    base = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), float(w.scale))
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps, e0.elapsed_time(e1) / args.steps
+
+    ms_dec, ev_dec = timed(lambda: bs.bsattn_fwd_decode(plan.handle, *base, ws.data_ptr(), nws, stream.cuda_stream))
+    ms_fwd, ev_fwd = timed(lambda: bs.bsattn_fwd(plan.handle, *base, stream.cuda_stream))
+    chunk, topk = int(w.k_offsets[1] - w.k_offsets[0]), int(w.sel_row_ptr[1] - w.sel_row_ptr[0])
+    kv_bytes = w.B * w.Hkv * topk * chunk * w.d * 2 * 2   # selected K and V rows, once per KV group
+    nbytes = kv_bytes + 2 * w.B * w.Nq * w.Hq * w.d * 2 + w.B * w.Hq * w.Nq * 4
+    log(f"[bench] decode {ms_dec:.3f} ms (events {ev_dec:.3f}); plain forward over the same plan {ms_fwd:.3f} ms")
+    out = {
+        "metric": "decode HBM GB/s (selected K/V read once per KV group), 1 GPU",
+        "value": round(nbytes / (ms_dec * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_dec, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16 Q/K/V)",
+        "config": {"workload": w.name, "pass": "decode", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq,
+                   "Nk": w.Nk, "d": w.d, "chunk": chunk, "topk": topk, "useful_pairs": st["useful"],
+                   "bytes": nbytes, "plain_forward_ms": round(ms_fwd, 4),
+                   "speedup_over_plain_forward": round(ms_fwd / ms_dec, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / (ev_dec * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(nbytes / (ev_dec * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "fwd_decode_kernel<128> + decode_merge_kernel<128>", "kernel_ms": round(ev_dec, 4)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -233,6 +298,8 @@ def main():
                     help="dispatch Q tiles in Q-block order, ignoring the workload's locality hint")
     ap.add_argument("--fixed-tiles", action="store_true",
                     help="plan with the fixed-tile baseline (one 128x128 tile per selected block pair, no packing)")
+    ap.add_argument("--decode", action="store_true",
+                    help="time the head-stacked decode path on the chunk-indexed long context instead")
     ap.add_argument("--chunk-select", action="store_true",
                     help="time the chunk selection instead (default workload then 5: chunk-indexed GQA prefill)")
     ap.add_argument("--bwd", action="store_true",
@@ -264,6 +331,9 @@ def main():
         args.workload = 4 if args.bwd else (5 if args.chunk_select else 3)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.decode:
+        bench_decode(args, dev)
+        return
     t0 = time.perf_counter()
     w = make(args.workload)
     log(f"[bench] workload {w.name}: inputs generated in {time.perf_counter() - t0:.1f} s")

@@ -292,7 +292,7 @@ int decode_geometry(const bsattn_plan* plan, int32_t* n_splits, int32_t* pps, si
   for (size_t r = 0; r + 1 < plan->pl_ptr.size(); ++r) max_list = std::max(max_list, plan->pl_ptr[r + 1] - plan->pl_ptr[r]);
   const int64_t items = int64_t(pr.B) * pr.Hkv * plan->n_qt[1];
   int64_t ns = items > 0 ? (2048 + items - 1) / items : 1;
-  ns = std::max<int64_t>(1, std::min<int64_t>(ns, (max_list + 7) / 8));
+  ns = std::max<int64_t>(1, std::min<int64_t>({ns, (max_list + 7) / 8, int64_t(256)}));
   int64_t per = (max_list + ns - 1) / ns;
   per = std::max<int64_t>(8, (per + 7) / 8 * 8);
   ns = std::max<int64_t>(1, (max_list + per - 1) / per);

@@ -42,8 +42,9 @@ struct DecCfg {
   static constexpr int kLds = kPages > kMerge ? kPages : kMerge;
 };
 
+// two waves per SIMD (two workgroups per CU): twice the loads in flight in this HBM-bound walk
 template <int D, bool KPERM>
-__global__ void __launch_bounds__(256) fwd_decode_kernel(DecodeParams p) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) fwd_decode_kernel(DecodeParams p) {
   using C = DecCfg<D>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kLds];
   uint8_t* sk = smem;
@@ -166,14 +167,17 @@ __global__ void __launch_bounds__(256) fwd_decode_kernel(DecodeParams p) {
     l_run *= alpha;
 #pragma unroll
     for (int db = 0; db < C::kDB; ++db) oacc[db] *= alpha;
-    float pe[16];
     bf16x8 pb[2];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], sl2, -m_use));
-      pb[e >> 3][e & 7] = (__bf16)pe[e];
+    for (int e = 0; e < 16; ++e) sacc[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], sl2, -m_use));
+#pragma unroll
+    for (int e = 0; e < 16; ++e) pb[e >> 3][e & 7] = (__bf16)sacc[e];
+    {
+      float tmp[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) tmp[e] = sacc[e];
+      l_run += sum16(tmp);
     }
-    l_run += sum16(pe);
     // O^T += V^T P^T
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -242,48 +246,57 @@ __global__ void __launch_bounds__(256) fwd_decode_kernel(DecodeParams p) {
   }
 }
 
-// one workgroup (256 threads) per (batch, KV group, Q block): 8 threads per stacked column
+// one workgroup (4 waves) per (batch, KV group, Q block, 4 stacked columns): a wave per
+// column, each lane D / 64 of its values
 template <int D>
 __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeParams p) {
-  const int item = blockIdx.x;  // (b * Hkv + g) * n_qtiles + t
+  constexpr int kPer = D / 64;
+  const int item = blockIdx.x >> 3;  // (b * Hkv + g) * n_qtiles + t
+  const int c = (blockIdx.x & 7) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int t = item % p.n_qtiles;
   const int bg = item / p.n_qtiles;
   const int b = bg / p.Hkv, g = bg - b * p.Hkv;
   const CONST_AS int32_t* qtiles = (const CONST_AS int32_t*)p.qtiles;
   const int row0 = qtiles[4 * t], n = qtiles[4 * t + 1];
-  const int c = threadIdx.x >> 3, part = threadIdx.x & 7;
-  if (c >= p.grp * n) return;
+  if (c >= p.grp * n) return;  // whole waves
   const int hi = c / n, qi = c - (c / n) * n;
   const int h = g * p.grp + hi;
   const int qslot = row0 + qi;
   const int qtok = p.qperm ? p.qperm[qslot] : qslot;
   const int64_t w0 = (int64_t)item * p.n_splits;
+  // split weights 2^(m_s - M): lanes over splits, wave reductions (n_splits <= 256)
+  __shared__ float sa[4][256];
+  float* wa = sa[threadIdx.x >> 6];
   float M = kNegInf;
-  for (int s = 0; s < p.n_splits; ++s) M = fmaxf(M, p.mlpart[((w0 + s) * 32 + c) * 2]);
+  for (int s = lane; s < p.n_splits; s += 64) M = fmaxf(M, p.mlpart[((w0 + s) * 32 + c) * 2]);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
   const float mu = M == kNegInf ? 0.f : M;
   float L = 0.f;
-  constexpr int kPer = D / 8;  // columns per thread
+  for (int s = lane; s < p.n_splits; s += 64) {
+    const float a = __builtin_amdgcn_exp2f(p.mlpart[((w0 + s) * 32 + c) * 2] - mu);
+    wa[s] = a;
+    L += a * p.mlpart[((w0 + s) * 32 + c) * 2 + 1];
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) L += __shfl_xor(L, m, 64);
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's LDS writes are visible to its own reads
   float acc[kPer];
 #pragma unroll
   for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
+#pragma unroll 8
   for (int s = 0; s < p.n_splits; ++s) {
-    const float a = __builtin_amdgcn_exp2f(p.mlpart[((w0 + s) * 32 + c) * 2] - mu);
-    L += a * p.mlpart[((w0 + s) * 32 + c) * 2 + 1];
-    const float* op = p.opart + ((w0 + s) * 32 + c) * D + part * kPer;
+    const float* op = p.opart + ((w0 + s) * 32 + c) * D + lane * kPer;
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) acc[e] += a * op[e];
+    for (int e = 0; e < kPer; ++e) acc[e] += wa[s] * op[e];
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   __bf16* dst = reinterpret_cast<__bf16*>(p.o) + (int64_t)b * p.o_sb + (int64_t)qtok * p.o_sn + (int64_t)h * p.o_sh +
-                part * kPer;
+                lane * kPer;
 #pragma unroll
-  for (int e = 0; e < kPer; e += 4) {
-    bf16x4 v4;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v4[j] = (__bf16)(acc[e + j] * inv);
-    *reinterpret_cast<bf16x4*>(dst + e) = v4;
-  }
-  if (part == 0)
+  for (int e = 0; e < kPer; ++e) dst[e] = (__bf16)(acc[e] * inv);
+  if (lane == 0)
     p.lse[((int64_t)b * p.Hq + h) * p.Nq + qtok] = L > 0.f ? (M + __log2f(L)) * 0.693147180559945309f : kNegInf;
 }
 
@@ -296,7 +309,7 @@ hipError_t launch_decode_d(const DecodeParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((fwd_decode_kernel<D, true>), dim3((unsigned)nwork), dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL((fwd_decode_kernel<D, false>), dim3((unsigned)nwork), dim3(256), 0, stream, p);
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)items), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)(items * 8)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
