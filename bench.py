@@ -267,9 +267,28 @@ def bench_decode(args, dev):
     ms_dec, ev_dec = timed(lambda: bs.bsattn_fwd_decode(plan.handle, *base, ws.data_ptr(), nws, stream.cuda_stream))
     ms_fwd, ev_fwd = timed(lambda: bs.bsattn_fwd(plan.handle, *base, stream.cuda_stream))
     chunk, topk = int(w.k_offsets[1] - w.k_offsets[0]), int(w.sel_row_ptr[1] - w.sel_row_ptr[0])
+
+    # the whole step on the device: chunk selection, page lists rebuilt from it, decode
+    cp = bs.ChunkProblem()
+    cp.B, cp.Hq, cp.Hkv, cp.Nq, cp.Nk, cp.d = w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d
+    cp.chunk, cp.topk, cp.query_index, cp.reserved = chunk, topk, w.Nq - 1, 0
+    cp.q_stride[:] = tuple(q.stride()[:3])
+    cp.k_stride[:] = tuple(k.stride()[:3])
+    summ = torch.empty((w.B, w.Hkv, -(-w.Nk // chunk), w.d), dtype=torch.float32, device=dev)
+    chunks = torch.empty((w.B, w.Hkv, topk), dtype=torch.int32, device=dev)
+    rp = torch.arange(0, w.B * w.Hkv * topk + 1, topk, dtype=torch.int32, device=dev)
+
+    def pipeline():
+        bs.bsattn_chunk_select(cp, q.data_ptr(), k.data_ptr(), summ.data_ptr(), chunks.data_ptr(), stream.cuda_stream)
+        bs.bsattn_plan_update_selection(plan.handle, w.B, w.Hkv, rp.data_ptr(), chunks.data_ptr(), 0,
+                                        stream.cuda_stream)
+        bs.bsattn_fwd_decode(plan.handle, *base, ws.data_ptr(), nws, stream.cuda_stream)
+
+    ms_pipe, _ = timed(pipeline)
     kv_bytes = w.B * w.Hkv * topk * chunk * w.d * 2 * 2   # selected K and V rows, once per KV group
     nbytes = kv_bytes + 2 * w.B * w.Nq * w.Hq * w.d * 2 + w.B * w.Hq * w.Nq * 4
-    log(f"[bench] decode {ms_dec:.3f} ms (events {ev_dec:.3f}); plain forward over the same plan {ms_fwd:.3f} ms")
+    log(f"[bench] decode {ms_dec:.3f} ms (events {ev_dec:.3f}); plain forward over the same plan {ms_fwd:.3f} ms; "
+        f"chunk selection + page lists on the device + decode {ms_pipe:.3f} ms")
     out = {
         "metric": "decode HBM GB/s (selected K/V read once per KV group), 1 GPU",
         "value": round(nbytes / (ms_dec * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -278,7 +297,8 @@ def bench_decode(args, dev):
         "config": {"workload": w.name, "pass": "decode", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq,
                    "Nk": w.Nk, "d": w.d, "chunk": chunk, "topk": topk, "useful_pairs": st["useful"],
                    "bytes": nbytes, "plain_forward_ms": round(ms_fwd, 4),
-                   "speedup_over_plain_forward": round(ms_fwd / ms_dec, 2)},
+                   "speedup_over_plain_forward": round(ms_fwd / ms_dec, 2),
+                   "device_step_ms": round(ms_pipe, 4)},
         "roofline": {"bound": "hbm", "achieved": round(nbytes / (ev_dec * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(nbytes / (ev_dec * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None,
                      "kernel": "fwd_decode_kernel<128> + decode_merge_kernel<128>", "kernel_ms": round(ev_dec, 4)},

@@ -21,7 +21,7 @@ __all__ = [
     "bsattn_plan_create", "bsattn_plan_create_ex", "bsattn_plan_set_block_order", "PLAN_FIXED_TILES", "bsattn_plan_device_bytes", "bsattn_plan_upload", "bsattn_plan_stats",
     "bsattn_plan_export", "bsattn_plan_export_bwd", "PlanBwdView", "bsattn_fwd", "bsattn_fwd_shape",
     "bsattn_bwd_workspace_bytes", "bsattn_bwd", "bsattn_chunk_select", "ChunkProblem", "chunk_select",
-    "bsattn_decode_workspace_bytes", "bsattn_fwd_decode",
+    "bsattn_decode_workspace_bytes", "bsattn_fwd_decode", "bsattn_plan_update_selection",
     "bsattn_plan_destroy", "bsattn_status_string", "bsattn_last_hip_error", "SHAPE_128x128", "SHAPE_64x256", "PAGE_SIZE",
 ]
 
@@ -95,7 +95,8 @@ _lib: Optional[ctypes.CDLL] = None
 EXPORTED = ["bsattn_plan_create", "bsattn_plan_create_ex", "bsattn_plan_set_block_order", "bsattn_plan_device_bytes", "bsattn_plan_upload", "bsattn_plan_stats",
             "bsattn_plan_export", "bsattn_plan_export_bwd", "bsattn_fwd", "bsattn_fwd_shape",
             "bsattn_bwd_workspace_bytes", "bsattn_bwd", "bsattn_chunk_select", "bsattn_decode_workspace_bytes",
-            "bsattn_fwd_decode", "bsattn_plan_destroy", "bsattn_status_string", "bsattn_last_hip_error"]
+            "bsattn_fwd_decode", "bsattn_plan_update_selection", "bsattn_plan_destroy", "bsattn_status_string",
+            "bsattn_last_hip_error"]
 
 
 def library() -> ctypes.CDLL:
@@ -124,6 +125,7 @@ def library() -> ctypes.CDLL:
     lib.bsattn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, ctypes.c_size_t, vp]
     lib.bsattn_decode_workspace_bytes.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t)]
     lib.bsattn_fwd_decode.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, ctypes.c_size_t, vp]
+    lib.bsattn_plan_update_selection.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp]
     lib.bsattn_chunk_select.argtypes = [ctypes.POINTER(ChunkProblem), vp, vp, vp, vp, vp]
     lib.bsattn_plan_destroy.argtypes = [vp]
     lib.bsattn_status_string.argtypes = [ctypes.c_int]
@@ -268,6 +270,14 @@ def bsattn_fwd_decode(plan, q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_
                                        ctypes.c_float(scale), vp(ws_ptr), ws_bytes, vp(stream)), "bsattn_fwd_decode")
 
 
+def bsattn_plan_update_selection(plan, n_b: int, n_h: int, row_ptr_ptr: int, kblk_ptr: int, status_ptr: int = 0,
+                                 stream: int = 0) -> None:
+    vp = ctypes.c_void_p
+    _check(library().bsattn_plan_update_selection(plan, n_b, n_h, vp(row_ptr_ptr), vp(kblk_ptr),
+                                                  vp(status_ptr) if status_ptr else None, vp(stream)),
+           "bsattn_plan_update_selection")
+
+
 def bsattn_chunk_select(problem: ChunkProblem, q_ptr: int, k_ptr: int, summ_ptr: int, chunks_ptr: int,
                         stream: int = 0) -> None:
     vp = ctypes.c_void_p
@@ -382,6 +392,19 @@ class Plan:
 
     def export_bwd(self) -> dict:
         return bsattn_plan_export_bwd(self.handle)
+
+    def update_selection(self, n_b, n_h, row_ptr, kblk, status=None, stream=None):
+        """Rebuild the page lists on the device from device int32 tensors (row_ptr, kblk);
+        ``status`` (a device int32 tensor of one element) collects the error bits."""
+        import torch
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        for name, t in (("row_ptr", row_ptr), ("kblk", kblk)):
+            if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+                raise BsattnError(1, f"update_selection: {name} must be a contiguous int32 device tensor")
+        bsattn_plan_update_selection(self.handle, n_b, n_h, row_ptr.data_ptr(), kblk.data_ptr(),
+                                     status.data_ptr() if status is not None else 0, stream)
+        return self
 
     def set_block_order(self, order):
         """Dispatch order of the Q blocks (a locality hint; upload afterwards)."""

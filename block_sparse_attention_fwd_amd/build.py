@@ -20,7 +20,7 @@ BUILD = os.path.join(PKG, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["plan.cpp", "api.cpp", "fwd_kernel.hip", "bwd_kernel.hip", "chunk_select.hip", "decode_kernel.hip"]
+SOURCES = ["plan.cpp", "api.cpp", "fwd_kernel.hip", "bwd_kernel.hip", "chunk_select.hip", "decode_kernel.hip", "plan_update.hip"]
 # packed-fp32 instructions are kept out of generated code (never emitted by hand either)
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

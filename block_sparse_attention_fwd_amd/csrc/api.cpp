@@ -15,6 +15,7 @@ hipError_t launch_fwd_shape(const FwdParams& p, int shape, int d, hipStream_t st
 hipError_t launch_bwd(const BwdParams& p, int d, hipStream_t stream);
 hipError_t launch_chunk_select(const ChunkParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t stream);
+hipError_t launch_plan_update(const PlanUpdateParams& p, hipStream_t stream);
 }
 
 namespace {
@@ -82,6 +83,31 @@ int bsattn_plan_upload(bsattn_plan* plan, void* dev, size_t bytes, void* stream)
                                 static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e);
   plan->dev = dev;
+  plan->updated_on_device = false;
+  return BSATTN_OK;
+}
+
+int bsattn_plan_update_selection(bsattn_plan* plan, int32_t n_b, int32_t n_h, const int32_t* row_ptr,
+                                 const int32_t* kblk, int32_t* status, void* stream) {
+  if (plan == nullptr || row_ptr == nullptr) return BSATTN_E_ARG;
+  if (plan->dev == nullptr) return BSATTN_E_STATE;
+  if (n_b != plan->sel_nb || n_h != plan->sel_nh) return BSATTN_E_ARG;
+  if (plan->flags != 0) return BSATTN_E_UNSUPPORTED;
+  uint8_t* base = static_cast<uint8_t*>(plan->dev);
+  bsattn::PlanUpdateParams up{};
+  up.row_ptr = row_ptr;
+  up.kblk = kblk;
+  up.first_page = reinterpret_cast<const int32_t*>(base + plan->off_firstpage);
+  up.page_ent = reinterpret_cast<const int32_t*>(base + plan->off_pageent);
+  up.pl_ptr = reinterpret_cast<int32_t*>(base + plan->off_plptr);
+  up.pl_ent = reinterpret_cast<int32_t*>(base + plan->off_plent);
+  up.status = status;
+  up.n_rows = int32_t(plan->pl_ptr.size()) - 1;
+  up.nkb = plan->nkb;
+  up.capacity = int32_t(plan->ent_capacity);
+  hipError_t e = bsattn::launch_plan_update(up, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  plan->updated_on_device = true;
   return BSATTN_OK;
 }
 
@@ -208,7 +234,7 @@ int run_bwd(const bsattn_plan* plan, const void* q, const void* k, const void* v
             const void* dout, void* dq, void* dk, void* dv, float scale, void* workspace, size_t workspace_bytes,
             void* stream) {
   if (plan == nullptr) return BSATTN_E_ARG;
-  if (plan->dev == nullptr) return BSATTN_E_STATE;
+  if (plan->dev == nullptr || plan->updated_on_device) return BSATTN_E_STATE;
   const bsattn_problem& pr = plan->prob;
   if (!std::isfinite(scale) || !(scale > 0.f)) return BSATTN_E_ARG;
   if (workspace == nullptr || workspace_bytes < bwd_workspace_bytes(pr) ||

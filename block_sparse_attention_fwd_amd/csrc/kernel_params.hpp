@@ -102,6 +102,18 @@ struct DecodeParams {
   float scale, scale_log2;
 };
 
+// Page lists rebuilt on the device from a device-resident selection.
+struct PlanUpdateParams {
+  const int32_t* row_ptr;     // [n_rows + 1] selection CSR (device)
+  const int32_t* kblk;        // selected K block ids, strictly ascending per row
+  const int32_t* first_page;  // [nkb + 1] first page of each K block
+  const int32_t* page_ent;    // [n_pages] packed page words
+  int32_t* pl_ptr;            // [n_rows + 1] row pointers of the plan
+  int32_t* pl_ent;            // [capacity] entries of the plan
+  int32_t* status;            // |= 1 capacity exceeded, 2 block id out of range, 4 row not ascending
+  int32_t n_rows, nkb, capacity;
+};
+
 // Chunk selection: summaries of key chunks and the top-k chunks per (batch, KV group).
 struct ChunkParams {
   const void* q;

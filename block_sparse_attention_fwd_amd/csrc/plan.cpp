@@ -307,6 +307,12 @@ int build_plan(const bsattn_problem& prob, const bsattn_layout& ql, const bsattn
   off = align256(off + sizeof(int32_t) * p->tpl_ptr.size());
   p->off_tplent = off;
   off = align256(off + sizeof(int32_t) * (p->tpl_pages.size() + kEntryPad));
+  // K layout tables for selection updates on the device
+  p->off_firstpage = off;
+  off = align256(off + sizeof(int32_t) * (size_t(nkb) + 1));
+  p->off_pageent = off;
+  off = align256(off + sizeof(int32_t) * p->page_kblock.size());
+  p->ent_capacity = int64_t(p->pl_pages.size());
   p->image.assign(std::max<size_t>(off, 256), 0);
 
   uint8_t* img = p->image.data();
@@ -336,6 +342,10 @@ int build_plan(const bsattn_problem& prob, const bsattn_layout& ql, const bsattn
   for (size_t t = 0; t < p->dqt_row0.size(); ++t) dqt[t] = QTileDev{p->dqt_row0[t], p->dqt_rows[t], p->dqt_qblock[t], 0};
   QTileDev* kvt = reinterpret_cast<QTileDev*>(img + p->off_kvt);
   for (size_t t = 0; t < p->kvt_row0.size(); ++t) kvt[t] = QTileDev{p->kvt_row0[t], p->kvt_rows[t], p->kvt_kblock[t], 0};
+  int32_t* fpg = reinterpret_cast<int32_t*>(img + p->off_firstpage);
+  for (int32_t kb = 0; kb <= nkb; ++kb) fpg[kb] = first_page[size_t(kb)];
+  int32_t* pgw = reinterpret_cast<int32_t*>(img + p->off_pageent);
+  for (size_t pg = 0; pg < p->page_kblock.size(); ++pg) pgw[pg] = (p->page_slot0[pg] << kEntryShift) | p->page_nvalid[pg];
   int32_t* tpp = reinterpret_cast<int32_t*>(img + p->off_tplptr);
   for (size_t r = 0; r < p->tpl_ptr.size(); ++r) tpp[r] = int32_t(p->tpl_ptr[r]);
   int32_t* tent = reinterpret_cast<int32_t*>(img + p->off_tplent);

@@ -60,6 +60,11 @@ struct bsattn_plan {
   std::vector<int64_t> tpl_ptr;
   std::vector<int32_t> tpl_pages;
   size_t off_dqt = 0, off_kvt = 0, off_tplptr = 0, off_tplent = 0;
+  // device-side selection updates: the K layout's first page per block and packed page
+  // words, the capacity of the entry array, and whether the lists were rebuilt on the device
+  size_t off_firstpage = 0, off_pageent = 0;
+  int64_t ent_capacity = 0;
+  bool updated_on_device = false;
   // bound device buffer (caller-owned)
   void* dev = nullptr;
 };

@@ -217,3 +217,11 @@ def test_decode_geometry_and_unsupported_plans():
     with pytest.raises(bs.BsattnError) as e:
         bs.bsattn_decode_workspace_bytes(bs.Plan.from_workload(per_head).handle)
     assert e.value.status == 4
+
+
+def test_update_selection_needs_upload():
+    w = make_random(12, B=1, Hq=2, Hkv=2, Nq=40, Nk=40, d=64, sel_mode="kv", with_tensors=False)
+    p = bs.Plan.from_workload(w)
+    with pytest.raises(bs.BsattnError) as e:
+        bs.bsattn_plan_update_selection(p.handle, w.sel_nb, w.sel_nh, 256, 256)
+    assert e.value.status == 7
