@@ -321,18 +321,31 @@ __global__ void __launch_bounds__(128) bwd_dq_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
-// dK, dV: one workgroup (2 waves) per (batch, KV head, 64-row K tile); the query heads of
+// dK, dV: one workgroup (4 waves) per (batch, KV head, 64-row K tile); the query heads of
 // the group are walked one after another, each over its unit's transposed page list.
+// Waves 0 and 1 (score waves) hold K^T and V^T of keys 0..31 and 32..63 in registers and
+// compute S and dP of each 32-query stage; they pass P^ and dS to LDS as bf16 B operands.
+// Waves 2 and 3 (gradient waves) hold the dK^T and dV^T accumulators of the same keys and
+// apply those operands one stage later.  Splitting the roles keeps every wave under 256
+// VGPRs, so two workgroups share a CU (two waves per SIMD) and each wave's phase hides the
+// other's latencies; the MFMA count per stage is the same as with one wave doing both.
+// Pipeline: score waves load the Q pages (and the row statistics), gradient waves the dO
+// pages, through registers, two stages ahead; Q and dO have three stage buffers (the score
+// waves read stage it while the gradient waves read stage it - 1 and stage it + 1 is
+// written), the operands two.  One barrier per iteration, the same count in both roles.
 template <int D, bool QPERM>
-__global__ void __launch_bounds__(128) bwd_dkdv_kernel(BwdParams p) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dkdv_kernel(BwdParams p) {
   using C = BwdCfg<D>;
-  __shared__ __attribute__((aligned(1024))) uint8_t sq[2 * C::kStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t sg[2 * C::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t sq[3 * C::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t sg[3 * C::kStage];
+  __shared__ __attribute__((aligned(16))) bf16x8 s_op[2][2][4][64];  // [stage & 1][key half][P^ 0, 1, dS 0, 1][lane]
   __shared__ __attribute__((aligned(16))) float s_lse[2][32];  // LSE in log2 units (+inf: no row)
   __shared__ __attribute__((aligned(16))) float s_d[2][32];
   __shared__ __attribute__((aligned(16))) int s_thr[2][32];    // causal bound of each query
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kh = wave & 1;     // key half; also the page of a stage this wave loads
+  const bool score = wave < 2;  // score wave (loads Q) or gradient wave (loads dO)
   const int hh = lane >> 5;
   const CONST_AS int32_t* tpl_ent = (const CONST_AS int32_t*)p.tpl_ent;
   const CONST_AS int32_t* tpl_ptr = (const CONST_AS int32_t*)p.tpl_ptr;
@@ -344,23 +357,11 @@ __global__ void __launch_bounds__(128) bwd_dkdv_kernel(BwdParams p) {
   const int b = bg / p.Hkv, g = bg - b * p.Hkv;
   const int slot0 = tiles[4 * t], rows = tiles[4 * t + 1], kblock = tiles[4 * t + 2];
 
-  // this lane's key: K^T and V^T B operands stay in registers
-  const int krow = wave * 32 + (lane & 31);
+  // this lane's key
+  const int krow = kh * 32 + (lane & 31);
   const bool kvalid = krow < rows;
   const int kslot = slot0 + (kvalid ? krow : 0);
   const int ktok = p.kperm ? p.kperm[kslot] : kslot;
-  bf16x8 kreg[C::kDS], vreg[C::kDS];
-  {
-    const __bf16* kp = reinterpret_cast<const __bf16*>(p.k) + (int64_t)b * p.k_sb + (int64_t)ktok * p.k_sn +
-                       (int64_t)g * p.k_sh + hh * 8;
-    const __bf16* vp = reinterpret_cast<const __bf16*>(p.v) + (int64_t)b * p.v_sb + (int64_t)ktok * p.v_sn +
-                       (int64_t)g * p.v_sh + hh * 8;
-#pragma unroll
-    for (int s = 0; s < C::kDS; ++s) {
-      kreg[s] = *reinterpret_cast<const bf16x8*>(kp + 16 * s);
-      vreg[s] = *reinterpret_cast<const bf16x8*>(vp + 16 * s);
-    }
-  }
 
   // stages: for each query head h of the group, ceil(pages / 2) stages of its list
   auto list_of = [&](int hi, int& a, int& z) {
@@ -375,6 +376,7 @@ __global__ void __launch_bounds__(128) bwd_dkdv_kernel(BwdParams p) {
     list_of(hi, a, z);
     nst += (z - a + 1) >> 1;
   }
+  const int n_it = nst > 0 ? nst + 1 : 0;  // the gradient waves run one stage behind
   // gather cursor: head index, next entry, end of its list (uniform); past the last list
   // it yields empty pages
   int c_h = 0, c_e = 0, c_z = 0;
@@ -382,8 +384,8 @@ __global__ void __launch_bounds__(128) bwd_dkdv_kernel(BwdParams p) {
 
   PageRows<D> pr;
   pr.init(lane);
-  // the next stage to load: its head, page entry, the tokens of this lane's load rows and
-  // the token of query row lane % 16 of the page (for the row statistics)
+  // the next stage to load: its head, this wave's page entry, the tokens of this lane's
+  // load rows and the token of query row lane % 16 of the page (for the row statistics)
   int n_h = 0, n_ent = 0, n_stok = 0;
   uint32_t tok[C::kInst];
   auto gather = [&]() {
@@ -392,43 +394,125 @@ __global__ void __launch_bounds__(128) bwd_dkdv_kernel(BwdParams p) {
       list_of(c_h, c_e, c_z);
     }
     n_h = c_h;
-    const int e = c_e + wave;
+    const int e = c_e + kh;
     n_ent = e < c_z ? tpl_ent[e] : 0;
     c_e += 2;
     pr.template gather<QPERM>(n_ent, p.qperm, tok);
-    const int r = lane & 15;
-    const int slot = ent_slot(n_ent) + (r < ent_nv(n_ent) ? r : 0);
-    n_stok = QPERM ? p.qperm[slot] : slot;
+    if (score) {
+      const int r = lane & 15;
+      const int slot = ent_slot(n_ent) + (r < ent_nv(n_ent) ? r : 0);
+      n_stok = QPERM ? p.qperm[slot] : slot;
+    }
   };
-  // the loaded stage, not yet in LDS: Q and dO rows and the row statistics
-  u32x4 rq[C::kInst], rg[C::kInst];
+  // the loaded page, not yet in LDS: Q (score waves) or dO (gradient waves) rows, and the
+  // row statistics (score waves)
+  u32x4 rr[C::kInst];
   float r_lse = 0.f, r_d = 0.f;
   int r_tok = 0, r_nv = 0;
   auto load = [&]() {
     const int h = g * p.grp + n_h;
-    const char* qslice = reinterpret_cast<const char*>(p.q) + ((int64_t)b * p.q_sb + (int64_t)h * p.q_sh) * 2;
-    const char* gslice = reinterpret_cast<const char*>(p.dout) + ((int64_t)b * p.o_sb + (int64_t)h * p.o_sh) * 2;
-    const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)qslice, (short)0, p.q_extent, 0x00020000);
-    const __amdgpu_buffer_rsrc_t grsrc = __builtin_amdgcn_make_buffer_rsrc((void*)gslice, (short)0, p.o_extent, 0x00020000);
-    pr.load(tok, qrsrc, p.q_sn_bytes, rq);
-    pr.load(tok, grsrc, p.o_sn_bytes, rg);
-    const int64_t idx = ((int64_t)b * p.Hq + h) * p.Nq + n_stok;
-    r_lse = p.lse[idx];
-    r_d = p.dvec[idx];
-    r_tok = n_stok;
-    r_nv = ent_nv(n_ent);
-  };
-  // wave w writes rows 16w .. 16w + 15; its lanes 0..15 the statistics of those rows
-  auto store = [&](int buf) {
-    pr.store(rq, sq + buf * C::kStage, wave, lane);
-    pr.store(rg, sg + buf * C::kStage, wave, lane);
-    if (lane < 16) {
-      const bool valid = lane < r_nv;
-      s_lse[buf][16 * wave + lane] = (valid && r_lse != kNegInf) ? r_lse * kLog2e : __builtin_huge_valf();
-      s_d[buf][16 * wave + lane] = valid ? r_d : 0.f;
-      s_thr[buf][16 * wave + lane] = causal_thr(p.q_pos0 + (int64_t)r_tok);
+    if (score) {
+      const char* qslice = reinterpret_cast<const char*>(p.q) + ((int64_t)b * p.q_sb + (int64_t)h * p.q_sh) * 2;
+      const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)qslice, (short)0, p.q_extent, 0x00020000);
+      pr.load(tok, qrsrc, p.q_sn_bytes, rr);
+      const int64_t idx = ((int64_t)b * p.Hq + h) * p.Nq + n_stok;
+      r_lse = p.lse[idx];
+      r_d = p.dvec[idx];
+      r_tok = n_stok;
+      r_nv = ent_nv(n_ent);
+    } else {
+      const char* gslice = reinterpret_cast<const char*>(p.dout) + ((int64_t)b * p.o_sb + (int64_t)h * p.o_sh) * 2;
+      const __amdgpu_buffer_rsrc_t grsrc = __builtin_amdgcn_make_buffer_rsrc((void*)gslice, (short)0, p.o_extent, 0x00020000);
+      pr.load(tok, grsrc, p.o_sn_bytes, rr);
     }
   };
+  // page kh of stage buffer `buf`: rows 16 kh .. 16 kh + 15; lanes 0..15 of a score wave
+  // write the statistics of those rows
+  auto store = [&](int buf, int sbuf) {
+    pr.store(rr, (score ? sq : sg) + buf * C::kStage, kh, lane);
+    if (score && lane < 16) {
+      const bool valid = lane < r_nv;
+      s_lse[sbuf][16 * kh + lane] = (valid && r_lse != kNegInf) ? r_lse * kLog2e : __builtin_huge_valf();
+      s_d[sbuf][16 * kh + lane] = valid ? r_d : 0.f;
+      s_thr[sbuf][16 * kh + lane] = causal_thr(p.q_pos0 + (int64_t)r_tok);
+    }
+  };
+
+  if (nst > 0) {
+    gather();
+    load();
+    store(0, 0);
+    gather();
+    load();
+    gather();
+  }
+
+  if (score) {
+    // K^T and V^T B operands of this lane's key
+    bf16x8 kreg[C::kDS], vreg[C::kDS];
+    {
+      const __bf16* kp = reinterpret_cast<const __bf16*>(p.k) + (int64_t)b * p.k_sb + (int64_t)ktok * p.k_sn +
+                         (int64_t)g * p.k_sh + hh * 8;
+      const __bf16* vp = reinterpret_cast<const __bf16*>(p.v) + (int64_t)b * p.v_sb + (int64_t)ktok * p.v_sn +
+                         (int64_t)g * p.v_sh + hh * 8;
+#pragma unroll
+      for (int s = 0; s < C::kDS; ++s) {
+        kreg[s] = *reinterpret_cast<const bf16x8*>(kp + 16 * s);
+        vreg[s] = *reinterpret_cast<const bf16x8*>(vp + 16 * s);
+      }
+    }
+    // settle these loads here: left in flight into the loop, they would make the loop's
+    // first use of them wait for every load outstanding there, prefetches included
+    wait_vmcnt<0>();
+    const float sl2 = p.scale_log2;
+    int cur = 0;  // Q/dO buffer of stage it
+    for (int it = 0; it < n_it; ++it) {
+      lds_barrier();  // stage it is in LDS; everybody is done with the buffers written next
+      if (it + 1 < nst) {
+        store(cur == 2 ? 0 : cur + 1, (it + 1) & 1);  // stage it + 1
+        load();                                       // stage it + 2
+        gather();                                     // tokens of stage it + 3
+      }
+      if (it < nst) {
+        const uint8_t* qb = sq + cur * C::kStage;
+        const uint8_t* gb = sg + cur * C::kStage;
+        f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+        for (int s = 0; s < C::kDS; ++s) {
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(qb, lane, s), kreg[s], sacc, 0, 0, 0);
+          dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(gb, lane, s), vreg[s], dpacc, 0, 0, 0);
+        }
+        // register i holds query 8 (i / 4) + 4 hh + i % 4 of the stage and this lane's key
+        const int sb = it & 1;
+        bf16x8 pb[2], dsb[2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 l4 = *reinterpret_cast<const float4*>(&s_lse[sb][8 * j + 4 * hh]);
+          const float4 d4 = *reinterpret_cast<const float4*>(&s_d[sb][8 * j + 4 * hh]);
+          int4 t4 = make_int4(0x7ffffffe, 0x7ffffffe, 0x7ffffffe, 0x7ffffffe);
+          if (p.causal) t4 = *reinterpret_cast<const int4*>(&s_thr[sb][8 * j + 4 * hh]);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+          const int tv[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * j + e;
+            float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], sl2, -lv[e]));
+            pv = ktok <= tv[e] ? pv : 0.f;
+            const float ds = pv * (dpacc[i] - dv[e]);
+            pb[i >> 3][i & 7] = (__bf16)pv;
+            dsb[i >> 3][i & 7] = (__bf16)ds;
+          }
+        }
+        s_op[sb][kh][0][lane] = pb[0];
+        s_op[sb][kh][1][lane] = pb[1];
+        s_op[sb][kh][2][lane] = dsb[0];
+        s_op[sb][kh][3][lane] = dsb[1];
+      }
+      cur = cur == 2 ? 0 : cur + 1;
+    }
+    return;
+  }
 
   f32x16 dkacc[C::kDB], dvacc[C::kDB];
 #pragma unroll
@@ -436,62 +520,33 @@ __global__ void __launch_bounds__(128) bwd_dkdv_kernel(BwdParams p) {
     dkacc[db] = f32x16{};
     dvacc[db] = f32x16{};
   }
-  const float sl2 = p.scale_log2;
-
-  if (nst > 0) {
-    gather();
-    load();
-    store(0);
-    gather();
-    load();
-    gather();
-  }
-  for (int st = 0; st < nst; ++st) {
-    const int buf = st & 1;
-    lds_barrier();  // stage st is in LDS; both waves are done with the other buffer
-    if (st + 1 < nst) {
-      store(buf ^ 1);  // stage st + 1
-      load();          // stage st + 2
-      gather();        // tokens of stage st + 3
+  int cur = 0;
+  for (int it = 0; it < n_it; ++it) {
+    lds_barrier();  // matches the score waves' barrier of the same iteration
+    if (it + 1 < nst) {
+      store(cur == 2 ? 0 : cur + 1, 0);
+      load();
+      gather();
     }
-    const uint8_t* qb = sq + buf * C::kStage;
-    const uint8_t* gb = sg + buf * C::kStage;
-
-    f32x16 sacc = f32x16{}, dpacc = f32x16{};
+    if (it >= 1) {  // stage it - 1
+      const int pb_ = cur == 0 ? 2 : cur - 1;
+      const uint8_t* qb = sq + pb_ * C::kStage;
+      const uint8_t* gb = sg + pb_ * C::kStage;
+      const int sb = (it - 1) & 1;
+      bf16x8 pb[2], dsb[2];
+      pb[0] = s_op[sb][kh][0][lane];
+      pb[1] = s_op[sb][kh][1][lane];
+      dsb[0] = s_op[sb][kh][2][lane];
+      dsb[1] = s_op[sb][kh][3][lane];
 #pragma unroll
-    for (int s = 0; s < C::kDS; ++s) {
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(qb, lane, s), kreg[s], sacc, 0, 0, 0);
-      dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(gb, lane, s), vreg[s], dpacc, 0, 0, 0);
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int db = 0; db < C::kDB; ++db) {
+          dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(gb, lane, half, db), pb[half], dvacc[db], 0, 0, 0);
+          dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(qb, lane, half, db), dsb[half], dkacc[db], 0, 0, 0);
+        }
     }
-
-    // register i holds query 8 (i / 4) + 4 hh + i % 4 of the stage and this lane's key
-    bf16x8 pb[2], dsb[2];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float4 l4 = *reinterpret_cast<const float4*>(&s_lse[buf][8 * j + 4 * hh]);
-      const float4 d4 = *reinterpret_cast<const float4*>(&s_d[buf][8 * j + 4 * hh]);
-      int4 t4 = make_int4(0x7ffffffe, 0x7ffffffe, 0x7ffffffe, 0x7ffffffe);
-      if (p.causal) t4 = *reinterpret_cast<const int4*>(&s_thr[buf][8 * j + 4 * hh]);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-      const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-      const int tv[4] = {t4.x, t4.y, t4.z, t4.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 4 * j + e;
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], sl2, -lv[e]));
-        pv = ktok <= tv[e] ? pv : 0.f;
-        const float ds = pv * (dpacc[i] - dv[e]);
-        pb[i >> 3][i & 7] = (__bf16)pv;
-        dsb[i >> 3][i & 7] = (__bf16)ds;
-      }
-    }
-#pragma unroll
-    for (int half = 0; half < 2; ++half)
-#pragma unroll
-      for (int db = 0; db < C::kDB; ++db) {
-        dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(gb, lane, half, db), pb[half], dvacc[db], 0, 0, 0);
-        dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(qb, lane, half, db), dsb[half], dkacc[db], 0, 0, 0);
-      }
+    cur = cur == 2 ? 0 : cur + 1;
   }
 
   if (!kvalid) return;
@@ -513,9 +568,9 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
   const int64_t n_kv = (int64_t)p.B * p.Hkv * p.n_kv_tiles;
   if (n_kv > 0) {
     if (p.qperm)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3((unsigned)n_kv), dim3(128), 0, stream, p);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3((unsigned)n_kv), dim3(256), 0, stream, p);
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3((unsigned)n_kv), dim3(128), 0, stream, p);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3((unsigned)n_kv), dim3(256), 0, stream, p);
   }
   const int64_t n_dq = (int64_t)p.B * p.Hq * p.n_dq_tiles;
   if (n_dq > 0) {
