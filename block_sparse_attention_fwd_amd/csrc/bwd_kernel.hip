@@ -193,10 +193,14 @@ __device__ __forceinline__ void store_rows(__bf16* dst, const f32x16 (&acc)[BwdC
 // ---------------------------------------------------------------------------------------
 // dQ: one workgroup (2 waves) per (batch, head, 64-row Q tile).
 template <int D, bool KPERM>
-__global__ void __launch_bounds__(128) bwd_dq_kernel(BwdParams p) {
+__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dq_kernel(BwdParams p) {
   using C = BwdCfg<D>;
-  __shared__ __attribute__((aligned(1024))) uint8_t sk[2 * C::kStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t sv[2 * C::kStage];
+  // the two stage buffers of K and of V as four objects, so that the compiler can tell the
+  // loads into one buffer from the reads of the other and waits only for the stage it reads
+  __shared__ __attribute__((aligned(1024))) uint8_t sk0[C::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t sk1[C::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t sv0[C::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t sv1[C::kStage];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hh = lane >> 5;
@@ -235,6 +239,8 @@ __global__ void __launch_bounds__(128) bwd_dq_kernel(BwdParams p) {
   // a row without keys has LSE = -inf: +inf here makes every probability exp2(-inf) = 0
   const float lse2 = lse == kNegInf ? __builtin_huge_valf() : lse * kLog2e;
   const float dval = p.dvec[(int64_t)bh * p.Nq + qtok];
+  // settled before the loop, so that no wait inside it has to cover them
+  wait_vmcnt<0>();
   const int thr = p.causal ? causal_thr(p.q_pos0 + (int64_t)qtok) : 0x7ffffffe;
 
   const char* kslice = reinterpret_cast<const char*>(p.k) + ((int64_t)b * p.k_sb + (int64_t)g * p.k_sh) * 2;
@@ -250,8 +256,8 @@ __global__ void __launch_bounds__(128) bwd_dq_kernel(BwdParams p) {
     pr.template gather<KPERM>(e < e1 ? pl_ent[e] : 0, p.kperm, tok);
     ++gst;
   };
-  auto fire = [&](int buf) {
-    pr.fire(tok, krsrc, p.k_sn_bytes, sk + buf * C::kStage, vrsrc, p.v_sn_bytes, sv + buf * C::kStage, wave);
+  auto fire = [&](uint8_t* kdst, uint8_t* vdst) __attribute__((always_inline)) {
+    pr.fire(tok, krsrc, p.k_sn_bytes, kdst, vrsrc, p.v_sn_bytes, vdst, wave);
   };
   // VMEM loads issued after a stage's pages by the time its wait runs: the next stage's
   // pages and, with a permutation, the gather of the stage after
@@ -262,16 +268,13 @@ __global__ void __launch_bounds__(128) bwd_dq_kernel(BwdParams p) {
   for (int db = 0; db < C::kDB; ++db) dqacc[db] = f32x16{};
   const float sl2 = p.scale_log2;
 
-  if (ns > 0) {
-    gather();
-    fire(0);
-    gather();
-  }
-  for (int st = 0; st < ns; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < ns) {
+  // stage st: its K and V pages are in kb / vb; the next stage's go to kn / vn
+  // (NEXT: a stage follows; known at compile time, so the steady state has no branch)
+  auto stage = [&](auto next_tag, int st, const uint8_t* kb, const uint8_t* vb, uint8_t* kn, uint8_t* vn)
+                   __attribute__((always_inline)) {
+    if constexpr (decltype(next_tag)::value) {
       lds_barrier();  // both waves are done with the other buffer (stage st - 1)
-      fire(buf ^ 1);  // stage st + 1
+      fire(kn, vn);   // stage st + 1
       gather();       // tokens of stage st + 2
       __builtin_amdgcn_sched_barrier(0);
       wait_vmcnt<kAfter>();  // stage st landed
@@ -279,8 +282,6 @@ __global__ void __launch_bounds__(128) bwd_dq_kernel(BwdParams p) {
       wait_vmcnt<0>();
     }
     lds_barrier();
-    const uint8_t* kb = sk + buf * C::kStage;
-    const uint8_t* vb = sv + buf * C::kStage;
 
     f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
@@ -293,26 +294,63 @@ __global__ void __launch_bounds__(128) bwd_dq_kernel(BwdParams p) {
     const int ea = e0 + 2 * st;
     const int ent0 = pl_ent[ea];
     const int ent1 = ea + 1 < e1 ? pl_ent[ea + 1] : 0;
+    // the products first, for every key: left to the compiler, the exponential would move
+    // under the mask test below and each key would become a branch
+    float dsv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dsv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], sl2, -lse2)) * (dpacc[i] - dval);
+      pin(dsv[i]);
+    }
+    // mask: rows past the page's valid count, and keys after the query under a causal mask
+    // (thr is INT_MAX - 1 without one); with permuted keys the causal test reads the key
+    // tokens, in a pass of its own so that the plain case stays free of branches
     bf16x8 dsb[2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int ent = (i >> 3) ? ent1 : ent0;
       const int rip = 8 * ((i >> 2) & 1) + 4 * hh + (i & 3);
       bool keep = rip < ent_nv(ent);
+      if constexpr (!KPERM) keep = keep & (ent_slot(ent) + rip <= thr);
+      dsb[i >> 3][i & 7] = (__bf16)(keep ? dsv[i] : 0.f);
+    }
+    if constexpr (KPERM) {
       if (p.causal) {
-        const int slot = ent_slot(ent) + rip;
-        const int ktok = KPERM ? p.kperm[keep ? slot : 0] : slot;
-        keep = keep && ktok <= thr;
+        int ktok[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ent = (i >> 3) ? ent1 : ent0;
+          const int rip = 8 * ((i >> 2) & 1) + 4 * hh + (i & 3);
+          ktok[i] = p.kperm[ent_slot(ent) + (rip < ent_nv(ent) ? rip : 0)];
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dsb[i >> 3][i & 7] = ktok[i] > thr ? (__bf16)0.f : dsb[i >> 3][i & 7];
       }
-      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], sl2, -lse2));
-      const float ds = keep ? pv * (dpacc[i] - dval) : 0.f;
-      dsb[i >> 3][i & 7] = (__bf16)ds;
     }
 #pragma unroll
     for (int half = 0; half < 2; ++half)
 #pragma unroll
       for (int db = 0; db < C::kDB; ++db)
         dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(kb, lane, half, db), dsb[half], dqacc[db], 0, 0, 0);
+    // each stage is scheduled on its own: no work moves between the two buffers' copies
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  if (ns > 0) {
+    gather();
+    fire(sk0, sv0);
+    gather();
+  }
+  int st = 0;
+  for (; st + 2 < ns; st += 2) {
+    stage(BoolTag<true>{}, st, sk0, sv0, sk1, sv1);
+    stage(BoolTag<true>{}, st + 1, sk1, sv1, sk0, sv0);
+  }
+  if (st + 1 < ns) {
+    stage(BoolTag<true>{}, st, sk0, sv0, sk1, sv1);
+    stage(BoolTag<false>{}, st + 1, sk1, sv1, sk0, sv0);
+  } else if (st < ns) {
+    stage(BoolTag<false>{}, st, sk0, sv0, sk1, sv1);
   }
 
   if (!qvalid) return;
