@@ -13,14 +13,15 @@
 // 16-row Q pages of every Q block that selects it, packed two per 32-query stage across Q
 // block boundaries as they are loaded into LDS.  A dQ workgroup owns 64 query slots of one
 // Q block and walks the forward's K page list of that block, two pages per 32-key stage.
-// Each wave holds 32 owned rows; the owned operands stay in registers and the streamed
+// Each wave works on 32 owned rows; the owned operands stay in registers and the streamed
 // side comes through LDS.  Every product is v_mfma_f32_32x32x16_bf16 with fp32
 // accumulation; P^ and dS are rounded to bf16 as MFMA operands.
 //
-// Per wave and stage (32 owned x 32 streamed rows, d = 128):
-//   dK/dV:  S = Q K^T, dP = dO V^T  (A = Q, dO rows from LDS; B = K^T, V^T in registers;
-//           each lane gets one key and 16 queries), then
-//           dV^T += dO^T P^, dK^T += Q^T dS  (A = dO^T, Q^T by transposing LDS reads)
+// Per stage (32 owned x 32 streamed rows, d = 128):
+//   dK/dV, score wave:    S = Q K^T, dP = dO V^T  (A = Q, dO rows from LDS; B = K^T, V^T in
+//                         registers; each lane gets one key and 16 queries), P^ and dS to LDS
+//   dK/dV, gradient wave: dV^T += dO^T P^, dK^T += Q^T dS  (A = dO^T, Q^T by transposing LDS
+//                         reads; B = P^, dS from LDS), one stage behind the score wave
 //   dQ:     S^T = K Q^T, dP^T = V dO^T (A = K, V rows; B = Q^T, dO^T in registers), then
 //           dQ^T += K^T dS^T (A = K^T by transposing LDS reads)
 #include <hip/hip_runtime.h>
@@ -93,7 +94,7 @@ __global__ void __launch_bounds__(256) bwd_dot_kernel(BwdParams p) {
 //
 // The dK/dV kernel stages pages through registers: the loads of stage st + 2 are issued while
 // stage st is computed and written to LDS in the next stage, so one barrier per stage
-// separates the writes of one buffer from the reads of the other.  The dQ kernel, which keeps
+// separates the writes of one buffer from the reads of the others.  The dQ kernel, which keeps
 // two waves per SIMD and has no registers to spare, loads pages straight into LDS one stage
 // ahead.  With a permuted layout the token gather runs one stage ahead of the loads, so no
 // load waits on a gather issued just before it.
