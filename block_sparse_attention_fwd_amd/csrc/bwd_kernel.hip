@@ -504,51 +504,75 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     // first use of them wait for every load outstanding there, prefetches included
     wait_vmcnt<0>();
     const float sl2 = p.scale_log2;
-    int cur = 0;  // Q/dO buffer of stage it
-    for (int it = 0; it < n_it; ++it) {
+    // per-lane byte offset of the A operand of k-step s inside a stage buffer (row lane % 32,
+    // logical chunk 2s + hh); the buffer itself is a compile-time offset (the loop below is
+    // unrolled over the three buffers), so no operand read needs an address instruction
+    uint32_t roff[C::kDS];
+    {
+      const int r = lane & 31;
+#pragma unroll
+      for (int s = 0; s < C::kDS; ++s) roff[s] = r * C::kRowBytes + (((2 * s + hh) ^ swz<D>(r)) * 16);
+    }
+    // iteration it with stage it in buffer B (compile-time)
+    auto iter = [&](auto buf_tag, int it) __attribute__((always_inline)) {
+      constexpr int B = decltype(buf_tag)::value;
       lds_barrier();  // stage it is in LDS; everybody is done with the buffers written next
       if (it + 1 < nst) {
-        store(cur == 2 ? 0 : cur + 1, (it + 1) & 1);  // stage it + 1
-        load();                                       // stage it + 2
-        gather();                                     // tokens of stage it + 3
+        store((B + 1) % 3, (it + 1) & 1);  // stage it + 1
+        load();                            // stage it + 2
+        gather();                          // tokens of stage it + 3
       }
       if (it < nst) {
-        const uint8_t* qb = sq + cur * C::kStage;
-        const uint8_t* gb = sg + cur * C::kStage;
+        const uint8_t* qb = sq + B * C::kStage;
+        const uint8_t* gb = sg + B * C::kStage;
         f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
         for (int s = 0; s < C::kDS; ++s) {
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(qb, lane, s), kreg[s], sacc, 0, 0, 0);
-          dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand<D>(gb, lane, s), vreg[s], dpacc, 0, 0, 0);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(qb + roff[s]), kreg[s], sacc, 0, 0, 0);
+          dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(gb + roff[s]), vreg[s], dpacc, 0, 0, 0);
         }
         // register i holds query 8 (i / 4) + 4 hh + i % 4 of the stage and this lane's key
         const int sb = it & 1;
-        bf16x8 pb[2], dsb[2];
+        float pv[16], dv[16];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float4 l4 = *reinterpret_cast<const float4*>(&s_lse[sb][8 * j + 4 * hh]);
           const float4 d4 = *reinterpret_cast<const float4*>(&s_d[sb][8 * j + 4 * hh]);
-          int4 t4 = make_int4(0x7ffffffe, 0x7ffffffe, 0x7ffffffe, 0x7ffffffe);
-          if (p.causal) t4 = *reinterpret_cast<const int4*>(&s_thr[sb][8 * j + 4 * hh]);
           const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-          const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-          const int tv[4] = {t4.x, t4.y, t4.z, t4.w};
+          const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int i = 4 * j + e;
-            float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], sl2, -lv[e]));
-            pv = ktok <= tv[e] ? pv : 0.f;
-            const float ds = pv * (dpacc[i] - dv[e]);
-            pb[i >> 3][i & 7] = (__bf16)pv;
-            dsb[i >> 3][i & 7] = (__bf16)ds;
+            pv[4 * j + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * j + e], sl2, -lv[e]));
+            dv[4 * j + e] = dd[e];
           }
+        }
+        // causal mask: a key after the query contributes nothing (without the mask, every
+        // key of a listed page row is kept; rows past a page's end already have P^ = 0)
+        if (p.causal) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int4 t4 = *reinterpret_cast<const int4*>(&s_thr[sb][8 * j + 4 * hh]);
+            const int tv[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pv[4 * j + e] = ktok <= tv[e] ? pv[4 * j + e] : 0.f;
+          }
+        }
+        bf16x8 pb[2], dsb[2];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          pb[i >> 3][i & 7] = (__bf16)pv[i];
+          dsb[i >> 3][i & 7] = (__bf16)(pv[i] * (dpacc[i] - dv[i]));
         }
         s_op[sb][kh][0][lane] = pb[0];
         s_op[sb][kh][1][lane] = pb[1];
         s_op[sb][kh][2][lane] = dsb[0];
         s_op[sb][kh][3][lane] = dsb[1];
       }
-      cur = cur == 2 ? 0 : cur + 1;
+    };
+    for (int it = 0; it < n_it; it += 3) {
+      iter(IntTag<0>{}, it);
+      if (it + 1 < n_it) iter(IntTag<1>{}, it + 1);
+      if (it + 2 < n_it) iter(IntTag<2>{}, it + 2);
     }
     return;
   }
