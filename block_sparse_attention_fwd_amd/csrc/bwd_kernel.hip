@@ -307,13 +307,19 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))
     // (thr is INT_MAX - 1 without one); with permuted keys the causal test reads the key
     // tokens, in a pass of its own so that the plain case stays free of branches
     bf16x8 dsb[2];
+    if (!p.causal && ent_nv(ent0) == 16 && ent_nv(ent1) == 16) {
+      // two full pages and no causal mask (the common stage): nothing to mask
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int ent = (i >> 3) ? ent1 : ent0;
-      const int rip = 8 * ((i >> 2) & 1) + 4 * hh + (i & 3);
-      bool keep = rip < ent_nv(ent);
-      if constexpr (!KPERM) keep = keep & (ent_slot(ent) + rip <= thr);
-      dsb[i >> 3][i & 7] = (__bf16)(keep ? dsv[i] : 0.f);
+      for (int i = 0; i < 16; ++i) dsb[i >> 3][i & 7] = (__bf16)dsv[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int ent = (i >> 3) ? ent1 : ent0;
+        const int rip = 8 * ((i >> 2) & 1) + 4 * hh + (i & 3);
+        bool keep = rip < ent_nv(ent);
+        if constexpr (!KPERM) keep = keep & (ent_slot(ent) + rip <= thr);
+        dsb[i >> 3][i & 7] = (__bf16)(keep ? dsv[i] : 0.f);
+      }
     }
     if constexpr (KPERM) {
       if (p.causal) {
