@@ -454,21 +454,35 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   u32x4 rr[C::kInst];
   float r_lse = 0.f, r_d = 0.f;
   int r_tok = 0, r_nv = 0;
+  // buffer resources of the current head's Q (or dO) slice and LSE / D rows, rebuilt only
+  // when the walk moves to the next head of the group (their 64-bit address arithmetic
+  // would otherwise cost a few dozen scalar instructions per stage)
+  int rs_h = -1;
+  __amdgpu_buffer_rsrc_t t_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p.q, (short)0, 0, 0x00020000);
+  __amdgpu_buffer_rsrc_t lse_rsrc = t_rsrc, d_rsrc = t_rsrc;
   auto load = [&]() {
-    const int h = g * p.grp + n_h;
+    if (n_h != rs_h) {
+      rs_h = n_h;
+      const int h = g * p.grp + n_h;
+      if (score) {
+        const char* qslice = reinterpret_cast<const char*>(p.q) + ((int64_t)b * p.q_sb + (int64_t)h * p.q_sh) * 2;
+        t_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)qslice, (short)0, p.q_extent, 0x00020000);
+        const int64_t srow = ((int64_t)b * p.Hq + h) * p.Nq;
+        lse_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(p.lse + srow), (short)0, (uint32_t)p.Nq * 4u, 0x00020000);
+        d_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(p.dvec + srow), (short)0, (uint32_t)p.Nq * 4u, 0x00020000);
+      } else {
+        const char* gslice = reinterpret_cast<const char*>(p.dout) + ((int64_t)b * p.o_sb + (int64_t)h * p.o_sh) * 2;
+        t_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)gslice, (short)0, p.o_extent, 0x00020000);
+      }
+    }
     if (score) {
-      const char* qslice = reinterpret_cast<const char*>(p.q) + ((int64_t)b * p.q_sb + (int64_t)h * p.q_sh) * 2;
-      const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)qslice, (short)0, p.q_extent, 0x00020000);
-      pr.load(tok, qrsrc, p.q_sn_bytes, rr);
-      const int64_t idx = ((int64_t)b * p.Hq + h) * p.Nq + n_stok;
-      r_lse = p.lse[idx];
-      r_d = p.dvec[idx];
+      pr.load(tok, t_rsrc, p.q_sn_bytes, rr);
+      r_lse = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lse_rsrc, n_stok * 4, 0, 0));
+      r_d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(d_rsrc, n_stok * 4, 0, 0));
       r_tok = n_stok;
       r_nv = ent_nv(n_ent);
     } else {
-      const char* gslice = reinterpret_cast<const char*>(p.dout) + ((int64_t)b * p.o_sb + (int64_t)h * p.o_sh) * 2;
-      const __amdgpu_buffer_rsrc_t grsrc = __builtin_amdgcn_make_buffer_rsrc((void*)gslice, (short)0, p.o_extent, 0x00020000);
-      pr.load(tok, grsrc, p.o_sn_bytes, rr);
+      pr.load(tok, t_rsrc, p.o_sn_bytes, rr);
     }
   };
   // page kh of stage buffer `buf`: rows 16 kh .. 16 kh + 15; lanes 0..15 of a score wave
