@@ -433,21 +433,38 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   // load rows and the token of query row lane % 16 of the page (for the row statistics)
   int n_h = 0, n_ent = 0, n_stok = 0;
   uint32_t tok[C::kInst];
-  auto gather = [&]() {
+  // The raw entry of a stage is fetched one gather before it is used, with a vector load:
+  // vector loads complete in order, so its use waits for it alone, while a scalar load can
+  // only be waited for together with every LDS access in flight (and the next LDS wait
+  // would take its whole latency).  Past its list the cursor reads entries it discards;
+  // the entry array is followed by 64 zero words, so the load stays in bounds.
+  const __amdgpu_buffer_rsrc_t ent_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.tpl_ent, (short)0, 0x7fffffff, 0x00020000);
+  int f_h = 0;
+  unsigned f_raw = 0;
+  bool f_ok = false;
+  auto fetch = [&]() {
     while (c_e >= c_z && c_h + 1 < p.grp) {
       ++c_h;
       list_of(c_h, c_e, c_z);
     }
-    n_h = c_h;
+    f_h = c_h;
     const int e = c_e + kh;
-    n_ent = e < c_z ? tpl_ent[e] : 0;
+    f_ok = e < c_z;
+    f_raw = __builtin_amdgcn_raw_buffer_load_b32(ent_rsrc, e * 4, 0, 0);
     c_e += 2;
+  };
+  auto gather = [&]() {
+    n_h = f_h;
+    n_ent = f_ok ? __builtin_amdgcn_readfirstlane((int)f_raw) : 0;
     pr.template gather<QPERM>(n_ent, p.qperm, tok);
     if (score) {
       const int r = lane & 15;
       const int slot = ent_slot(n_ent) + (r < ent_nv(n_ent) ? r : 0);
       n_stok = QPERM ? p.qperm[slot] : slot;
     }
+    __builtin_amdgcn_sched_barrier(0);
+    fetch();  // the stage after
   };
   // the loaded page, not yet in LDS: Q (score waves) or dO (gradient waves) rows, and the
   // row statistics (score waves)
@@ -498,6 +515,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   };
 
   if (nst > 0) {
+    fetch();
     gather();
     load();
     store(0, 0);
