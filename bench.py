@@ -39,21 +39,25 @@ SHORT_NAMES = {1: "tiny3d", 2: "onedim", 3: "videodit3d", 4: "partitions", 5: "c
 KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_fwd_amd", "csrc", "fwd_kernel.hip")
 
 
-def measured_traffic(workload, shape_tag):
-    """HBM bytes per launch (read + write) recorded by rocprofv3 counter runs in
-    profiles/traffic_<workload>.txt -- only while the kernel source is the one measured."""
+def measured_counters(workload):
+    """Per-launch figures recorded by rocprofv3 counter runs in profiles/traffic_<workload>.txt
+    (key = value lines), or {} unless the kernel source is the one measured."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"traffic_{SHORT_NAMES.get(workload, '')}.txt")
     if not os.path.exists(path):
-        return None
+        return {}
     kv = {}
     for line in open(path):
         if "=" in line and not line.lstrip().startswith("#"):
             key, val = line.split("=", 1)
             kv[key.strip()] = val.strip()
     sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-    if kv.get("source_sha256") != sha:
-        return None
+    return kv if kv.get("source_sha256") == sha else {}
+
+
+def measured_traffic(workload, shape_tag):
+    """HBM bytes per launch (read + write) from the counter runs, or None."""
+    kv = measured_counters(workload)
     try:
         return int(kv[f"{shape_tag}.read_bytes"]) + int(kv[f"{shape_tag}.write_bytes"])
     except KeyError:
@@ -406,18 +410,28 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    k128 = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    k64 = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    t128 = np.array([e[0].elapsed_time(e[1]) for e in events])
+    t64 = np.array([e[1].elapsed_time(e[2]) for e in events])
+    k128, k64 = float(np.mean(t128)), float(np.mean(t64))
     log(f"[bench] {ms_step:.3f} ms/step (wall); kernel 128x128 {k128:.3f} ms, kernel 64x256 {k64:.3f} ms")
 
     flop = 4.0 * w.d * st["useful"]
     value = flop / (ms_step * 1e-3) / 1e12
     u128 = st["useful_by_shape"][0]
     achieved = 4.0 * w.d * u128 / (k128 * 1e-3) / 1e12
+    traffic = measured_traffic(args.workload, "128x128")
+    kv = measured_counters(args.workload)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(args.workload, "128x128"),
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "kernel": f"fwd_kernel_pp<{w.d}> (128x128 tiles)", "kernel_ms": round(k128, 4),
-                "useful_pairs_per_launch": u128}
+                "useful_pairs_per_launch": u128,
+                # HBM rate of the counted bytes over this run's launch time, against 8 TB/s
+                "hbm_GBps": round(traffic / (k128 * 1e-3) / 1e9, 1) if traffic else None,
+                "hbm_frac": round(traffic / (k128 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) if traffic else None,
+                # from the same counter runs (MFMA busy share of active SIMD cycles, LDS bank-conflict cycles)
+                "mfma_busy_pct": float(kv["128x128.mfma_busy_pct"]) if "128x128.mfma_busy_pct" in kv else None,
+                "lds_bank_conflict_cycles": int(kv["128x128.lds_bank_conflict_cycles"])
+                if "128x128.lds_bank_conflict_cycles" in kv else None}
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -442,6 +456,11 @@ def main():
                    "physical_over_useful": round(st["physical"] / max(st["useful"], 1), 4),
                    "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
                    "kernel_ms": {"128x128": round(k128, 4), "64x256": round(k64, 4)},
+                   "kernel_ms_median": {"128x128": round(float(np.median(t128)), 4),
+                                        "64x256": round(float(np.median(t64)), 4)},
+                   "kernel_ms_min": {"128x128": round(float(np.min(t128)), 4), "64x256": round(float(np.min(t64)), 4)},
+                   "step_ms_median_events": round(float(np.median(t128 + t64)), 4),
+                   "step_ms_min_events": round(float(np.min(t128 + t64)), 4),
                    "plan": "fixed 128x128 tiles per selected block pair (no packing)" if args.fixed_tiles
                    else "packed pages, routed Q tiles",
                    "dispatch_order": "Q blocks in order" if (args.natural_order or w.q_block_order is None)
@@ -451,7 +470,9 @@ def main():
         "cpu_baseline": cpu,
     }
     if args.fixed_tiles or args.natural_order:
-        roofline["traffic"] = None  # the counter runs cover the default plan and order only
+        # the counter runs cover the default plan and order only
+        for key in ("traffic", "hbm_GBps", "hbm_frac", "mfma_busy_pct", "lds_bank_conflict_cycles"):
+            roofline[key] = None
     print(json.dumps(out), flush=True)
 
 
