@@ -193,3 +193,22 @@ def test_bwd_partitions_full_size_sampled():
     check_grad(dq[0, qtoks, h], rq, "partitions dQ rows")
     check_grad(dk[0, ktoks, h], rk, "partitions dK cluster")
     check_grad(dv[0, ktoks, h], rv, "partitions dV cluster")
+
+
+def test_bwd_videodit_full_size_sampled():
+    # video-DiT 3D at full size (75,600 tokens, 40 heads, cube layout): dQ of sampled queries
+    # and dK/dV of every key of one cube, in one head, against the oracle
+    w = make(3)
+    _say(f"[gpu-bwd] video-DiT full size: Nq={w.Nq} Hq={w.Hq} d={w.d}")
+    dq, dk, dv, plan = run_gpu_bwd(w)
+    assert np.all(np.isfinite(dq)) and np.all(np.isfinite(dk)) and np.all(np.isfinite(dv))
+    rng = np.random.default_rng(3)
+    h = 29
+    qtoks = np.sort(rng.choice(w.Nq, 48, replace=False))
+    kb = int(rng.integers(0, w.n_kblocks))
+    ktoks = np.arange(w.k_offsets[kb], w.k_offsets[kb + 1])
+    _say(f"[gpu-bwd] oracle: {len(qtoks)} query rows and cube {kb} ({len(ktoks)} keys) of head {h}")
+    (rq,), ((rk, rv),) = masked_attention_bwd_w(w, draw_dout(w), q_rows=[(0, h, qtoks)], k_rows=[(0, h, ktoks)])
+    check_grad(dq[0, qtoks, h], rq, "video-DiT dQ rows")
+    check_grad(dk[0, ktoks, h], rk, "video-DiT dK cube")
+    check_grad(dv[0, ktoks, h], rv, "video-DiT dV cube")
