@@ -392,7 +392,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int kh = wave & 1;     // key half; also the page of a stage this wave loads
   const bool score = wave < 2;  // score wave (loads Q) or gradient wave (loads dO)
   const int hh = lane >> 5;
-  const CONST_AS int32_t* tpl_ent = (const CONST_AS int32_t*)p.tpl_ent;
   const CONST_AS int32_t* tpl_ptr = (const CONST_AS int32_t*)p.tpl_ptr;
   const CONST_AS int32_t* tiles = (const CONST_AS int32_t*)p.kv_tiles;
 
