@@ -259,6 +259,8 @@ int run_bwd(const bsattn_plan* plan, const void* q, const void* k, const void* v
   const int64_t n_dq = int64_t(pr.B) * pr.Hq * int64_t(plan->dqt_row0.size());
   const int64_t n_kv = int64_t(pr.B) * pr.Hkv * int64_t(plan->kvt_row0.size());
   if (n_dq >= (int64_t(1) << 31) || n_kv >= (int64_t(1) << 31)) return BSATTN_E_UNSUPPORTED;
+  // the dK/dV kernel reads the transposed page entries through 32-bit byte offsets
+  if (plan->tpl_pages.size() + bsattn::kEntryPad >= (size_t(1) << 29)) return BSATTN_E_UNSUPPORTED;
 
   const uint8_t* base = static_cast<const uint8_t*>(plan->dev);
   bsattn::BwdParams bp{};

@@ -260,8 +260,9 @@ int bsattn_bwd_workspace_bytes(const bsattn_plan* plan, size_t* bytes);
  * produced by the one workgroup that owns its key, each dQ row by the one that owns its
  * query: no atomics, and the result is the same on every call.  Asynchronous on stream; no
  * allocation, no synchronisation.  The Q and dO rows of one (batch, query head) must lie
- * within 4 GiB of the slice's first element, like K and V (BSATTN_E_UNSUPPORTED
- * otherwise).  Q, K, V and dO must be finite in every row of their layouts.  Errors as for
+ * within 4 GiB of the slice's first element, like K and V, and the plan's transposed page
+ * lists (bsattn_plan_export_bwd) must hold fewer than 2^29 - 64 entries
+ * (BSATTN_E_UNSUPPORTED otherwise).  Q, K, V and dO must be finite in every row of their layouts.  Errors as for
  * bsattn_fwd; a missing or short workspace is BSATTN_E_ARG. */
 int bsattn_bwd(const bsattn_plan* plan, const void* q, const void* k, const void* v, const void* o,
                const float* lse, const void* dout, void* dq, void* dk, void* dv, float scale,
