@@ -100,6 +100,8 @@ int build_plan(const bsattn_problem& prob, const bsattn_layout& ql, const bsattn
   if (sel.row_ptr == nullptr) return BSATTN_E_ARG;
   const int64_t n_units = int64_t(sel.n_b) * sel.n_h;
   const int64_t n_rows = n_units * nqb;
+  // kernels index the (unit, block) row pointers of either side with 32-bit arithmetic
+  if (n_rows >= (int64_t(1) << 31) - 1 || n_units * nkb >= (int64_t(1) << 31) - 1) return BSATTN_E_UNSUPPORTED;
   if (sel.row_ptr[0] != 0) return BSATTN_E_SELECTION;
   for (int64_t r = 0; r < n_rows; ++r)
     if (sel.row_ptr[r + 1] < sel.row_ptr[r]) return BSATTN_E_SELECTION;
