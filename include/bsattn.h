@@ -157,7 +157,10 @@ typedef struct bsattn_plan bsattn_plan;
 
 /* Build a plan on the host: validate, cut K blocks into pages, route Q blocks into
  * tiles, build the page lists and the pair counts.  page_size must be 16.  On success
- * *out owns a new plan (free it with bsattn_plan_destroy); on failure *out is NULL. */
+ * *out owns a new plan (free it with bsattn_plan_destroy); on failure *out is NULL.
+ * Limits (BSATTN_E_UNSUPPORTED past them): B * Hq <= 2^24; selection units times Q blocks,
+ * and selection units times K blocks, below 2^31 - 1; page lists (forward and transposed)
+ * below 2^31 entries. */
 int bsattn_plan_create(const bsattn_problem* problem, const bsattn_layout* q_layout,
                        const bsattn_layout* k_layout, const bsattn_selection* selection,
                        int32_t page_size, bsattn_plan** out);
