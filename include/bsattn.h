@@ -158,7 +158,7 @@ typedef struct bsattn_plan bsattn_plan;
 /* Build a plan on the host: validate, cut K blocks into pages, route Q blocks into
  * tiles, build the page lists and the pair counts.  page_size must be 16.  On success
  * *out owns a new plan (free it with bsattn_plan_destroy); on failure *out is NULL.
- * Limits (BSATTN_E_UNSUPPORTED past them): B * Hq <= 2^24; selection units times Q blocks,
+ * Limits (BSATTN_E_UNSUPPORTED past them): Nq, Nk < 2^26; B * Hq <= 2^24; selection units times Q blocks,
  * and selection units times K blocks, below 2^31 - 1; page lists (forward and transposed)
  * below 2^31 entries. */
 int bsattn_plan_create(const bsattn_problem* problem, const bsattn_layout* q_layout,
