@@ -83,7 +83,6 @@ int bsattn_plan_upload(bsattn_plan* plan, void* dev, size_t bytes, void* stream)
                                 static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e);
   plan->dev = dev;
-  plan->updated_on_device = false;
   return BSATTN_OK;
 }
 
@@ -105,9 +104,15 @@ int bsattn_plan_update_selection(bsattn_plan* plan, int32_t n_b, int32_t n_h, co
   up.n_rows = int32_t(plan->pl_ptr.size()) - 1;
   up.nkb = plan->nkb;
   up.capacity = int32_t(plan->ent_capacity);
+  up.first_qpage = reinterpret_cast<const int32_t*>(base + plan->off_firstqpage);
+  up.qpage_ent = reinterpret_cast<const int32_t*>(base + plan->off_qpageent);
+  up.tpl_ptr = reinterpret_cast<int32_t*>(base + plan->off_tplptr);
+  up.tpl_ent = reinterpret_cast<int32_t*>(base + plan->off_tplent);
+  up.n_units = plan->n_units;
+  up.nqb = plan->nqb;
+  up.tcapacity = int32_t(plan->tent_capacity);
   hipError_t e = bsattn::launch_plan_update(up, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e);
-  plan->updated_on_device = true;
   return BSATTN_OK;
 }
 
@@ -234,7 +239,7 @@ int run_bwd(const bsattn_plan* plan, const void* q, const void* k, const void* v
             const void* dout, void* dq, void* dk, void* dv, float scale, void* workspace, size_t workspace_bytes,
             void* stream) {
   if (plan == nullptr) return BSATTN_E_ARG;
-  if (plan->dev == nullptr || plan->updated_on_device) return BSATTN_E_STATE;
+  if (plan->dev == nullptr) return BSATTN_E_STATE;
   const bsattn_problem& pr = plan->prob;
   if (!std::isfinite(scale) || !(scale > 0.f)) return BSATTN_E_ARG;
   if (workspace == nullptr || workspace_bytes < bwd_workspace_bytes(pr) ||

@@ -112,6 +112,12 @@ struct PlanUpdateParams {
   int32_t* pl_ent;            // [capacity] entries of the plan
   int32_t* status;            // |= 1 capacity exceeded, 2 block id out of range, 4 row not ascending
   int32_t n_rows, nkb, capacity;
+  // transposed lists (backward): Q pages per (unit, K block), Q blocks ascending
+  const int32_t* first_qpage; // [nqb + 1] first page of each Q block
+  const int32_t* qpage_ent;   // [n_qpages] packed Q page words
+  int32_t* tpl_ptr;           // [n_units * nkb + 1]
+  int32_t* tpl_ent;           // [tcapacity]
+  int32_t n_units, nqb, tcapacity;
 };
 
 // Chunk selection: summaries of key chunks and the top-k chunks per (batch, KV group).

@@ -314,6 +314,11 @@ int build_plan(const bsattn_problem& prob, const bsattn_layout& ql, const bsattn
   off = align256(off + sizeof(int32_t) * (size_t(nkb) + 1));
   p->off_pageent = off;
   off = align256(off + sizeof(int32_t) * p->page_kblock.size());
+  p->off_firstqpage = off;
+  off = align256(off + sizeof(int32_t) * (size_t(nqb) + 1));
+  p->off_qpageent = off;
+  off = align256(off + sizeof(int32_t) * p->qpage_qblock.size());
+  p->tent_capacity = int64_t(p->tpl_pages.size());
   p->ent_capacity = int64_t(p->pl_pages.size());
   p->image.assign(std::max<size_t>(off, 256), 0);
 
@@ -355,6 +360,10 @@ int build_plan(const bsattn_problem& prob, const bsattn_layout& ql, const bsattn
     const int32_t pg = p->tpl_pages[e];
     tent[e] = (p->qpage_slot0[pg] << kEntryShift) | p->qpage_nvalid[pg];
   }
+  int32_t* fqp = reinterpret_cast<int32_t*>(img + p->off_firstqpage);
+  for (int32_t qb = 0; qb <= nqb; ++qb) fqp[qb] = first_qpage[size_t(qb)];
+  int32_t* qpw = reinterpret_cast<int32_t*>(img + p->off_qpageent);
+  for (size_t pg = 0; pg < p->qpage_qblock.size(); ++pg) qpw[pg] = (p->qpage_slot0[pg] << kEntryShift) | p->qpage_nvalid[pg];
   return BSATTN_OK;
 }
 

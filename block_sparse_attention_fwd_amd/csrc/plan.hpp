@@ -61,10 +61,13 @@ struct bsattn_plan {
   std::vector<int32_t> tpl_pages;
   size_t off_dqt = 0, off_kvt = 0, off_tplptr = 0, off_tplent = 0;
   // device-side selection updates: the K layout's first page per block and packed page
-  // words, the capacity of the entry array, and whether the lists were rebuilt on the device
+  // words, and the capacity of the entry array
   size_t off_firstpage = 0, off_pageent = 0;
   int64_t ent_capacity = 0;
-  bool updated_on_device = false;
+  // the same for the transposed lists: the Q layout's first page per block, packed Q page
+  // words, and the capacity of the transposed entry array
+  size_t off_firstqpage = 0, off_qpageent = 0;
+  int64_t tent_capacity = 0;
   // bound device buffer (caller-owned)
   void* dev = nullptr;
 };

@@ -1,6 +1,6 @@
 // Page lists rebuilt on the device from a device-resident block selection (a selection that
 // changes every step, e.g. the chunks chosen by bsattn_chunk_select), without a host round
-// trip.  The rules are the host planner's: each (unit, Q block) row lists the pages of its
+// trip; the backward's transposed lists are rebuilt after them.  The rules are the host planner's: each (unit, Q block) row lists the pages of its
 // selected K blocks, blocks ascending, pages ascending, packed as (first slot << 5) | valid
 // rows, and every 4-entry stage (from the row's start) that holds a partial page or is cut
 // short by the row's end carries bit 31 (KPage abstract, zhuanzhiai page 1, sentences 2 and
@@ -39,29 +39,56 @@ __global__ void __launch_bounds__(256) plan_count_kernel(PlanUpdateParams p) {
   if (lane == 0) p.pl_ptr[r + 1] = (int32_t)(n < 0x7fffffff ? n : 0x7fffffff);
 }
 
-// exclusive prefix sum of the counts, clamped to the capacity (one workgroup)
+// exclusive prefix sum of the counts, clamped to the capacity (one workgroup): tiles of
+// 4096 counts, four consecutive per thread (coalesced), scanned within each wave by shuffles
+// and across the 16 waves through LDS, with the running total carried from tile to tile
 __global__ void __launch_bounds__(1024) plan_scan_kernel(PlanUpdateParams p) {
-  __shared__ int64_t part[1024];
-  const int tid = threadIdx.x;
-  const int per = (p.n_rows + 1023) / 1024;
-  const int r0 = min(p.n_rows, tid * per), r1 = min(p.n_rows, r0 + per);
-  int64_t local = 0;
-  for (int r = r0; r < r1; ++r) local += p.pl_ptr[r + 1];
-  part[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int64_t v = tid >= off ? part[tid - off] : 0;
+  __shared__ int64_t wsum[16];
+  __shared__ int64_t s_carry;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int64_t carry = 0;
+  for (int base = 0; base < p.n_rows; base += 4096) {
+    int64_t v[4], tot = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = base + 4 * tid + i;
+      v[i] = r < p.n_rows ? p.pl_ptr[r + 1] : 0;
+      tot += v[i];
+    }
+    int64_t incl = tot;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int64_t x = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += x;
+    }
+    if (lane == 63) wsum[w] = incl;
     __syncthreads();
-    part[tid] += v;
+    if (w == 0) {
+      const int64_t x = lane < 16 ? wsum[lane] : 0;
+      int64_t xi = x;
+#pragma unroll
+      for (int d = 1; d < 16; d <<= 1) {
+        const int64_t y = __shfl_up(xi, d, 64);
+        if (lane >= d) xi += y;
+      }
+      if (lane < 16) wsum[lane] = xi - x;  // exclusive wave offsets
+    }
     __syncthreads();
+    int64_t run = carry + wsum[w] + incl - tot;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = base + 4 * tid + i;
+      run += v[i];
+      if (r < p.n_rows) p.pl_ptr[r + 1] = (int32_t)(run < p.capacity ? run : p.capacity);
+    }
+    if (tid == 1023) s_carry = run;  // the tile's running total
+    __syncthreads();
+    carry = s_carry;
   }
-  int64_t run = part[tid] - local;
-  for (int r = r0; r < r1; ++r) {
-    run += p.pl_ptr[r + 1];
-    p.pl_ptr[r + 1] = (int32_t)(run < p.capacity ? run : p.capacity);
+  if (tid == 0) {
+    p.pl_ptr[0] = 0;
+    if (carry > p.capacity) flag(p, 1);
   }
-  if (tid == 0) p.pl_ptr[0] = 0;
-  if (tid == 1023 && part[1023] > p.capacity) flag(p, 1);
 }
 
 // entries: one wave per row, lanes over the row's blocks 64 at a time
@@ -109,12 +136,117 @@ __global__ void __launch_bounds__(256) plan_flag_kernel(PlanUpdateParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Transposed lists for the backward: for each (unit, K block), the Q pages of every Q block
+// whose selection row holds the K block -- Q blocks ascending, pages ascending -- the order
+// the host planner uses, so the backward walks the same pairs in the same order.  A wave
+// takes one list, its lanes test 64 Q blocks at a time (binary search in the block's
+// ascending selection row), and a lane prefix sum places each member's pages.
+
+// whether K block kb is in the ascending row kblk[a, b)
+__device__ __forceinline__ bool row_has(const int32_t* kblk, int a, int b, int kb) {
+  while (a < b) {
+    const int m = (a + b) >> 1;
+    const int v = kblk[m];
+    if (v == kb) return true;
+    if (v < kb) a = m + 1;
+    else b = m;
+  }
+  return false;
+}
+
+// Q pages that list t = unit * nkb + kb receives from Q block qb (0 when qb does not select kb)
+__device__ __forceinline__ int tpl_pages_of(const PlanUpdateParams& p, int t, int qb) {
+  if (qb >= p.nqb) return 0;
+  const int unit = t / p.nkb, kb = t - unit * p.nkb;
+  const int row = unit * p.nqb + qb;
+  return row_has(p.kblk, p.row_ptr[row], p.row_ptr[row + 1], kb) ? p.first_qpage[qb + 1] - p.first_qpage[qb] : 0;
+}
+
+// entries of each transposed list into tpl_ptr[t + 1]: one wave per list
+__global__ void __launch_bounds__(256) tpl_count_kernel(PlanUpdateParams p) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= p.n_units * p.nkb) return;
+  int64_t n = 0;
+  for (int qb0 = 0; qb0 < p.nqb; qb0 += 64) n += tpl_pages_of(p, t, qb0 + lane);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) n += __shfl_xor(n, m, 64);
+  if (lane == 0) p.tpl_ptr[t + 1] = (int32_t)(n < 0x7fffffff ? n : 0x7fffffff);
+}
+
+// the same with one thread per list, for plans of few Q blocks (a decode or prefill block
+// per unit), where a wave per list would leave most lanes idle
+__global__ void __launch_bounds__(256) tpl_count_small_kernel(PlanUpdateParams p) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= p.n_units * p.nkb) return;
+  int64_t n = 0;
+  for (int qb = 0; qb < p.nqb; ++qb) n += tpl_pages_of(p, t, qb);
+  p.tpl_ptr[t + 1] = (int32_t)(n < 0x7fffffff ? n : 0x7fffffff);
+}
+
+__global__ void __launch_bounds__(256) tpl_fill_small_kernel(PlanUpdateParams p) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= p.n_units * p.nkb) return;
+  const int base = p.tpl_ptr[t], end = p.tpl_ptr[t + 1];
+  int pos = base;
+  for (int qb = 0; qb < p.nqb; ++qb) {
+    const int np = tpl_pages_of(p, t, qb);
+    for (int i = 0; i < np; ++i, ++pos)
+      if (pos < end) p.tpl_ent[pos] = p.qpage_ent[p.first_qpage[qb] + i];
+  }
+}
+
+// the entries: one wave per list, lanes over its Q blocks 64 at a time
+__global__ void __launch_bounds__(256) tpl_fill_kernel(PlanUpdateParams p) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= p.n_units * p.nkb) return;
+  const int base = p.tpl_ptr[t], end = p.tpl_ptr[t + 1];
+  int run = 0;
+  for (int qb0 = 0; qb0 < p.nqb; qb0 += 64) {
+    const int qb = qb0 + lane;
+    const int np = tpl_pages_of(p, t, qb);
+    int incl = np;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += v;
+    }
+    const int pos0 = base + run + incl - np;
+    for (int i = 0; i < np; ++i) {
+      const int pos = pos0 + i;
+      if (pos < end) p.tpl_ent[pos] = p.qpage_ent[p.first_qpage[qb] + i];
+    }
+    run += __shfl(incl, 63, 64);
+  }
+}
+
 hipError_t launch_plan_update(const PlanUpdateParams& p, hipStream_t stream) {
   if (p.n_rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(plan_count_kernel, dim3((p.n_rows + 3) / 4), dim3(256), 0, stream, p);
   hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, stream, p);
   hipLaunchKernelGGL(plan_fill_kernel, dim3((p.n_rows + 3) / 4), dim3(256), 0, stream, p);
   hipLaunchKernelGGL(plan_flag_kernel, dim3((p.n_rows + 3) / 4), dim3(256), 0, stream, p);
+  const int64_t n_lists = int64_t(p.n_units) * p.nkb;
+  if (p.tpl_ptr != nullptr && n_lists > 0) {
+    // the transposed lists: count, prefix sum (the same scan, clamped to their capacity), fill
+    PlanUpdateParams t = p;
+    t.pl_ptr = p.tpl_ptr;
+    t.n_rows = int32_t(n_lists);
+    t.capacity = p.tcapacity;
+    if (p.nqb <= 16) {
+      const unsigned grid = (unsigned)((n_lists + 255) / 256);
+      hipLaunchKernelGGL(tpl_count_small_kernel, dim3(grid), dim3(256), 0, stream, t);
+      hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, stream, t);
+      hipLaunchKernelGGL(tpl_fill_small_kernel, dim3(grid), dim3(256), 0, stream, t);
+    } else {
+      const unsigned grid = (unsigned)((n_lists + 3) / 4);
+      hipLaunchKernelGGL(tpl_count_kernel, dim3(grid), dim3(256), 0, stream, t);
+      hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, stream, t);
+      hipLaunchKernelGGL(tpl_fill_kernel, dim3(grid), dim3(256), 0, stream, t);
+    }
+  }
   return hipGetLastError();
 }
 

@@ -202,16 +202,18 @@ int bsattn_plan_upload(bsattn_plan* plan, void* dev, size_t bytes, void* stream)
 /* Rebuild the plan's page lists on the device from a device-resident selection (a mask
  * that changes every step, such as the chunks of bsattn_chunk_select), asynchronously on
  * stream, with the host planner's rules (selected blocks ascending, pages ascending, stage
- * flags).  n_b and n_h must match the plan's selection; row_ptr [n_b * n_h * n_qblocks + 1]
- * and kblk are device int32 arrays, each row strictly ascending (bsattn_chunk_select's
- * output is).  The lists may hold at most as many pages as the selection the plan was created
- * with (its page_list_len); longer lists are cut at that capacity.  status, if not NULL, is a
- * device int32 that the update ORs with 1 (capacity exceeded), 2 (a block id out of range,
+ * flags), then the backward's transposed lists (for each unit and K block, the Q pages of
+ * the Q blocks that select it, Q blocks ascending).  n_b and n_h must match the plan's
+ * selection; row_ptr [n_b * n_h * n_qblocks + 1] and kblk are device int32 arrays, each row
+ * strictly ascending (bsattn_chunk_select's output is).  Each set of lists may hold at most
+ * as many entries as it held for the selection the plan was created with (page_list_len for
+ * the forward lists); longer lists are cut at that capacity.  status, if not NULL, is a
+ * device int32 that the update ORs with 1 (a capacity exceeded), 2 (a block id out of range,
  * skipped) or 4 (a row not strictly ascending); the caller clears it.  Afterwards bsattn_fwd,
- * bsattn_fwd_shape and bsattn_fwd_decode use the new lists (calls ordered on the stream);
- * the host-side statistics and exported arrays keep the creation selection, and bsattn_bwd
- * returns BSATTN_E_STATE until bsattn_plan_upload restores the creation selection.
- * BSATTN_E_UNSUPPORTED for a plan made with flags. */
+ * bsattn_fwd_shape, bsattn_fwd_decode and bsattn_bwd use the new lists (calls ordered on
+ * the stream); the host-side statistics and exported arrays keep the creation selection.
+ * bsattn_plan_upload restores the creation selection.  BSATTN_E_UNSUPPORTED for a plan made
+ * with flags. */
 int bsattn_plan_update_selection(bsattn_plan* plan, int32_t n_b, int32_t n_h, const int32_t* row_ptr,
                                  const int32_t* kblk, int32_t* status, void* stream);
 

@@ -2,8 +2,9 @@
 the float64 oracle.
 
 A plan created with one selection and updated on the device with another must run exactly
-like a plan built on the host for the second selection: the forward outputs are compared
-bit for bit (same lists, same work order), and against the oracle at the forward's bar.
+like a plan built on the host for the second selection: the forward outputs and the
+backward's gradients are compared bit for bit (same lists, same work order), and the
+forward against the oracle at the forward's bar.
 Error bits: capacity exceeded, block id out of range, row not ascending.
 """
 import sys
@@ -77,10 +78,14 @@ def test_device_update_equals_host_plan(seed, perm, causal, decode):
     err = np.abs(O[live] - Or[live])
     _say(f"update seed {seed}: O max {err.max():.3e} mean {err.mean():.3e}")
     assert err.max() <= 2e-2 and err.mean() <= 1e-3 and np.abs(L[live] - Lr[live]).max() <= 1e-3
-    # the backward keeps the creation selection's lists: refused until a fresh upload
-    with pytest.raises(bs.BsattnError) as e:
-        a.bwd(q, k, v, oa, la, q)
-    assert e.value.status == 7
+    # the backward walks the device-built transposed lists: bitwise the host plan's gradients
+    # (dO: any bf16 tensor in O's layout)
+    ga = a.bwd(q, k, v, oa, la, q, scale=w2.scale)
+    gb = b.bwd(q, k, v, ob, lb, q, scale=w2.scale)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    for name, x, y in zip(("dQ", "dK", "dV"), ga, gb):
+        assert torch.equal(x, y), f"{name} from the device-built lists differs from the host plan's"
     a.upload(a.device_buffer)
     oc, lc = run(a)
     o1, l1 = run(bs.Plan.from_workload(w1).upload())
