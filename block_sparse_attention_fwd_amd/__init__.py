@@ -394,8 +394,9 @@ class Plan:
         return bsattn_plan_export_bwd(self.handle)
 
     def update_selection(self, n_b, n_h, row_ptr, kblk, status=None, stream=None):
-        """Rebuild the page lists on the device from device int32 tensors (row_ptr, kblk);
-        ``status`` (a device int32 tensor of one element) collects the error bits."""
+        """Rebuild the page lists (the forward's and the backward's transposed ones) on the
+        device from device int32 tensors (row_ptr, kblk); ``status`` (a device int32 tensor of
+        one element) collects the error bits."""
         import torch
         if stream is None:
             stream = torch.cuda.current_stream().cuda_stream
