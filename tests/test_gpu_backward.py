@@ -212,3 +212,27 @@ def test_bwd_videodit_full_size_sampled():
     check_grad(dq[0, qtoks, h], rq, "video-DiT dQ rows")
     check_grad(dk[0, ktoks, h], rk, "video-DiT dK cube")
     check_grad(dv[0, ktoks, h], rv, "video-DiT dV cube")
+
+
+def test_bwd_chunk_gqa_full_size_sampled():
+    # chunk-indexed GQA prefill at full size (4 x 262,144 keys, 64 query heads in 8 KV groups,
+    # causal): dQ of sampled query rows against the oracle (each reaches its group's 131,072
+    # selected keys), and exact zeros in dK/dV for chunks that a group does not select
+    w = make(5)
+    _say(f"[gpu-bwd] chunk GQA full size: B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Nk={w.Nk} causal={w.causal}")
+    dq, dk, dv, plan = run_gpu_bwd(w)
+    assert np.all(np.isfinite(dq)) and np.all(np.isfinite(dk)) and np.all(np.isfinite(dv))
+    rng = np.random.default_rng(5)
+    b, h = 2, 45
+    qtoks = np.sort(rng.choice(w.Nq, 12, replace=False))
+    _say(f"[gpu-bwd] oracle: {len(qtoks)} query rows of (batch {b}, head {h})")
+    (rq,), _ = masked_attention_bwd_w(w, draw_dout(w), q_rows=[(b, h, qtoks)])
+    check_grad(dq[b, qtoks, h], rq, "chunk GQA dQ rows")
+    g = h // (w.Hq // w.Hkv)
+    assert w.n_qblocks == 1 and w.sel_nb == w.B and w.sel_nh == w.Hkv  # one query block, a selection per (b, g)
+    unit = b * w.sel_nh + g
+    selected = set(int(c) for c in w.sel_kblk[w.sel_row_ptr[unit]:w.sel_row_ptr[unit + 1]])
+    unselected = [c for c in range(w.n_kblocks) if c not in selected][:64]
+    for c in unselected:
+        sl = slice(int(w.k_offsets[c]), int(w.k_offsets[c + 1]))
+        assert not dk[b, sl, g].any() and not dv[b, sl, g].any(), f"dK/dV of unselected chunk {c}"
