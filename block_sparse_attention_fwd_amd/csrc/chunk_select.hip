@@ -20,24 +20,38 @@
 
 namespace bsattn {
 
-// summaries: one wave per (b, g, chunk); lane (r, col) sums rows t = r (mod 64 / (D / 8)) of
-// the chunk over 8 columns from 16-byte loads, then the row groups are combined by shuffles
+// summaries: one wave per (b, chunk, g), g fastest, so that the waves of a workgroup and
+// neighbouring workgroups read adjacent head slices of the same key rows (whole rows of the
+// usual [B, N, H, d] layout stream through together).  Lane (r, col) sums rows
+// t = r (mod 64 / (D / 8)) of the chunk over 8 columns from 16-byte loads, four loads in
+// flight per step; the row groups are then combined by shuffles.
 template <int D>
 __global__ void __launch_bounds__(256) chunk_summary_kernel(ChunkParams p) {
   constexpr int L = D / 8;     // lanes per row
   constexpr int RPI = 64 / L;  // rows per load instruction
   const int lane = threadIdx.x & 63;
-  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b * Hkv + g) * n_chunks + c
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b * n_chunks + c) * Hkv + g
   if (item >= (int64_t)p.B * p.Hkv * p.n_chunks) return;  // whole waves leave together
-  const int c = (int)(item % p.n_chunks);
-  const int64_t bg = item / p.n_chunks;
-  const int64_t b = bg / p.Hkv, g = bg - b * p.Hkv;
+  const int g = (int)(item % p.Hkv);
+  const int64_t bc = item / p.Hkv;
+  const int64_t b = bc / p.n_chunks;
+  const int c = (int)(bc - b * p.n_chunks);
   const int t0 = c * p.chunk;
   const int t1 = min(p.Nk, t0 + p.chunk);
   const int col = (lane % L) * 8, r = lane / L;
   const __bf16* base = reinterpret_cast<const __bf16*>(p.k) + b * p.k_sb + g * p.k_sh + col;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int t = t0 + r; t < t1; t += RPI) {
+  int t = t0 + r;
+  for (; t + 3 * RPI < t1; t += 4 * RPI) {
+    bf16x8 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const bf16x8*>(base + (int64_t)(t + u * RPI) * p.k_sn);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += (float)v[u][e];
+  }
+  for (; t < t1; t += RPI) {
     const bf16x8 v = *reinterpret_cast<const bf16x8*>(base + (int64_t)t * p.k_sn);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] += (float)v[e];
@@ -48,7 +62,7 @@ __global__ void __launch_bounds__(256) chunk_summary_kernel(ChunkParams p) {
     for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], m, 64);
   if (r == 0) {
     const float inv = 1.f / (float)(t1 - t0);
-    float* dst = p.summ + item * D + col;
+    float* dst = p.summ + ((b * p.Hkv + g) * p.n_chunks + c) * D + col;
     *reinterpret_cast<float4*>(dst) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
     *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
   }
@@ -76,19 +90,40 @@ __global__ void __launch_bounds__(1024) chunk_topk_kernel(ChunkParams p) {
     iq[tid] = s / (float)p.grp;
   }
   __syncthreads();
+  // scores, coalesced: D/4 lanes read one summary row (16 bytes each) and reduce its dot
+  // product by shuffles; every wave keeps U rows' loads in flight.
   // key = (descending score, ascending id): ~(order-preserving score bits) << 32 | id
-  for (int c = tid; c < npad; c += 1024) {
-    uint64_t key = ~uint64_t(0);
-    if (c < n) {
-      const float* sm = p.summ + ((int64_t)bg * n + c) * D;
-      float s = 0.f;
-#pragma unroll 8
-      for (int e = 0; e < D; ++e) s = __builtin_fmaf(sm[e], iq[e], s);
-      const uint32_t u = __float_as_uint(s);
-      const uint32_t ord = (u >> 31) ? ~u : (u | 0x80000000u);
-      key = (uint64_t(~ord) << 32) | uint32_t(c);
+  {
+    constexpr int LPR = D / 4, RPI = 64 / LPR, U = 4;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int sub = lane / LPR, e0 = (lane % LPR) * 4;
+    const float q0 = iq[e0], q1 = iq[e0 + 1], q2 = iq[e0 + 2], q3 = iq[e0 + 3];
+    const float* srow = p.summ + (int64_t)bg * n * D + e0;
+    for (int cb = wave * RPI * U; cb < npad; cb += 16 * RPI * U) {
+      float s[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = cb + u * RPI + sub;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (c < n) v = *reinterpret_cast<const float4*>(srow + (int64_t)c * D);
+        s[u] = __builtin_fmaf(v.w, q3, __builtin_fmaf(v.z, q2, __builtin_fmaf(v.y, q1, v.x * q0)));
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int m = 1; m < LPR; m <<= 1) s[u] += __shfl_xor(s[u], m, 64);
+        const int c = cb + u * RPI + sub;
+        if (lane % LPR == 0 && c < npad) {
+          uint64_t key = ~uint64_t(0);
+          if (c < n) {
+            const uint32_t w = __float_as_uint(s[u]);
+            const uint32_t ord = (w >> 31) ? ~w : (w | 0x80000000u);
+            key = (uint64_t(~ord) << 32) | uint32_t(c);
+          }
+          keys[c] = key;
+        }
+      }
     }
-    keys[c] = key;
   }
   __syncthreads();
   // bitonic sort, ascending
