@@ -91,10 +91,10 @@ __global__ void __launch_bounds__(1024) chunk_topk_kernel(ChunkParams p) {
   }
   __syncthreads();
   // scores, coalesced: D/4 lanes read one summary row (16 bytes each) and reduce its dot
-  // product by shuffles; every wave keeps U rows' loads in flight.
+  // product by shuffles; every wave keeps U loads (U * 64 / (D / 4) rows) in flight.
   // key = (descending score, ascending id): ~(order-preserving score bits) << 32 | id
   {
-    constexpr int LPR = D / 4, RPI = 64 / LPR, U = 4;
+    constexpr int LPR = D / 4, RPI = 64 / LPR, U = 8;
     const int lane = tid & 63, wave = tid >> 6;
     const int sub = lane / LPR, e0 = (lane % LPR) * 4;
     const float q0 = iq[e0], q1 = iq[e0 + 1], q2 = iq[e0 + 2], q3 = iq[e0 + 3];
@@ -126,20 +126,67 @@ __global__ void __launch_bounds__(1024) chunk_topk_kernel(ChunkParams p) {
     }
   }
   __syncthreads();
-  // bitonic sort, ascending
-  for (int k = 2; k <= npad; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < npad; i += 1024) {
-        const int l = i ^ j;
-        if (l > i) {
-          const uint64_t a = keys[i], c2 = keys[l];
-          const bool up = (i & k) == 0;
-          if ((a > c2) == up) {
-            keys[i] = c2;
-            keys[l] = a;
-          }
+  // bitonic sort, ascending.  Element i of the network lives in LDS, except during the stages
+  // whose partner distance j is below 64: then lane i % 64 of wave (i / 64) % 16 holds it in
+  // register i / 1024 and takes the partner's key by a lane shuffle, so those stages need no
+  // barrier (21 of the 78 stages of 4096 keys go through LDS).
+  {
+    constexpr int RMAX = kMaxChunks / 1024;
+    const int nreg = npad >= 1024 ? npad / 1024 : 1;
+    uint64_t a[RMAX];
+    auto reg_load = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int r = 0; r < RMAX; ++r) {
+        const int i = tid + 1024 * r;
+        if (r < nreg) a[r] = i < npad ? keys[i] : ~uint64_t(0);
+      }
+    };
+    auto reg_store = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int r = 0; r < RMAX; ++r) {
+        const int i = tid + 1024 * r;
+        if (r < nreg && i < npad) keys[i] = a[r];
+      }
+    };
+    // every lane of the workgroup runs the shuffles (nreg is uniform); lanes past npad hold
+    // dummies whose partners are dummies too (npad is a power of two and j < npad)
+    auto reg_stage = [&](int k, int j) __attribute__((always_inline)) {
+#pragma unroll
+      for (int r = 0; r < RMAX; ++r) {
+        if (r < nreg) {
+          const int i = tid + 1024 * r;
+          const int lo = __shfl_xor((int)(uint32_t)a[r], j, 64);
+          const int hi = __shfl_xor((int)(uint32_t)(a[r] >> 32), j, 64);
+          const uint64_t o = (uint64_t(uint32_t(hi)) << 32) | uint32_t(lo);
+          const bool up = (i & k) == 0, lower = (i & j) == 0;
+          const uint64_t mn = a[r] < o ? a[r] : o, mx = a[r] < o ? o : a[r];
+          a[r] = lower == up ? mn : mx;
         }
       }
+    };
+    reg_load();
+    for (int k = 2; k <= min(64, npad); k <<= 1)
+      for (int j = k >> 1; j > 0; j >>= 1) reg_stage(k, j);
+    reg_store();
+    __syncthreads();
+    for (int k = 128; k <= npad; k <<= 1) {
+      for (int j = k >> 1; j >= 64; j >>= 1) {
+        for (int i = tid; i < npad; i += 1024) {
+          const int l = i ^ j;
+          if (l > i) {
+            const uint64_t x = keys[i], y = keys[l];
+            const bool up = (i & k) == 0;
+            if ((x > y) == up) {
+              keys[i] = y;
+              keys[l] = x;
+            }
+          }
+        }
+        __syncthreads();
+      }
+      reg_load();
+      for (int j = 32; j > 0; j >>= 1) reg_stage(k, j);
+      reg_store();
       __syncthreads();
     }
   }
