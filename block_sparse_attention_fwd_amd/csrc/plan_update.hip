@@ -5,7 +5,8 @@
 // rows, and every 4-entry stage (from the row's start) that holds a partial page or is cut
 // short by the row's end carries bit 31 (KPage abstract, zhuanzhiai page 1, sentences 2 and
 // 4).  Four small kernels: page counts per row, a prefix sum into the row pointers (clamped
-// to the entry capacity), the entries, the stage flags.
+// to the entry capacity), the entries, the stage flags; a wave per row, or a workgroup per
+// row when the rows are fewer than the CUs.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -39,51 +40,102 @@ __global__ void __launch_bounds__(256) plan_count_kernel(PlanUpdateParams p) {
   if (lane == 0) p.pl_ptr[r + 1] = (int32_t)(n < 0x7fffffff ? n : 0x7fffffff);
 }
 
-// exclusive prefix sum of the counts, clamped to the capacity (one workgroup): tiles of
-// 4096 counts, four consecutive per thread (coalesced), scanned within each wave by shuffles
-// and across the 16 waves through LDS, with the running total carried from tile to tile
+// The same counts for plans with few long rows (fewer rows than CUs, e.g. one Q block per
+// sequence and KV group over thousands of chunks): a 1024-thread workgroup per row.
+__global__ void __launch_bounds__(1024) plan_count_wide_kernel(PlanUpdateParams p) {
+  __shared__ int64_t part[16];
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int j0 = p.row_ptr[r], j1 = p.row_ptr[r + 1];
+  int64_t n = 0;
+  for (int j = j0 + tid; j < j1; j += 1024) {
+    const int kb = p.kblk[j];
+    if (kb < 0 || kb >= p.nkb) {
+      flag(p, 2);
+      continue;
+    }
+    if (j > j0 && kb <= p.kblk[j - 1]) flag(p, 4);
+    n += p.first_page[kb + 1] - p.first_page[kb];
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) n += __shfl_xor(n, m, 64);
+  if (lane == 0) part[w] = n;
+  __syncthreads();
+  if (tid == 0) {
+    int64_t t = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t += part[i];
+    p.pl_ptr[r + 1] = (int32_t)(t < 0x7fffffff ? t : 0x7fffffff);
+  }
+}
+
+// exclusive prefix sum of the counts, clamped to the capacity (one workgroup).  A tile of
+// 16384 counts is four groups of 4096; in each group a thread takes four consecutive counts
+// (every load and store instruction covers 1 KB), the groups are scanned within each wave by
+// shuffles, and one 64-lane scan in wave 0 orders the 4 x 16 wave totals (lane 16 h + w:
+// group h, wave w).  The running total is carried from tile to tile.
 __global__ void __launch_bounds__(1024) plan_scan_kernel(PlanUpdateParams p) {
-  __shared__ int64_t wsum[16];
-  __shared__ int64_t s_carry;
+  constexpr int kGroups = 4, kTile = 4096 * kGroups;
+  __shared__ int64_t wsum[64];
+  __shared__ int64_t s_tot;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int64_t carry = 0;
-  for (int base = 0; base < p.n_rows; base += 4096) {
-    int64_t v[4], tot = 0;
+  for (int64_t base = 0; base < p.n_rows; base += kTile) {
+    int32_t v[kGroups][4];
+    int64_t tot[kGroups], incl[kGroups];
+    // unconditional loads (slots past the end read the last count and are zeroed), so that
+    // all sixteen are in flight together instead of one branch and one wait each
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = base + 4 * tid + i;
-      v[i] = r < p.n_rows ? p.pl_ptr[r + 1] : 0;
-      tot += v[i];
+    for (int h = 0; h < kGroups; ++h) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t r = base + 4096 * h + 4 * tid + i;
+        const int32_t x = p.pl_ptr[(r < p.n_rows ? r : p.n_rows - 1) + 1];
+        v[h][i] = r < p.n_rows ? x : 0;
+      }
     }
-    int64_t incl = tot;
+#pragma unroll
+    for (int h = 0; h < kGroups; ++h) {
+      tot[h] = (int64_t)v[h][0] + v[h][1] + v[h][2] + v[h][3];
+      incl[h] = tot[h];
+    }
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
-      const int64_t x = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += x;
+#pragma unroll
+      for (int h = 0; h < kGroups; ++h) {
+        const int64_t x = __shfl_up(incl[h], d, 64);
+        if (lane >= d) incl[h] += x;
+      }
     }
-    if (lane == 63) wsum[w] = incl;
+    if (lane == 63) {
+#pragma unroll
+      for (int h = 0; h < kGroups; ++h) wsum[16 * h + w] = incl[h];
+    }
     __syncthreads();
     if (w == 0) {
-      const int64_t x = lane < 16 ? wsum[lane] : 0;
+      const int64_t x = wsum[lane];
       int64_t xi = x;
 #pragma unroll
-      for (int d = 1; d < 16; d <<= 1) {
+      for (int d = 1; d < 64; d <<= 1) {
         const int64_t y = __shfl_up(xi, d, 64);
         if (lane >= d) xi += y;
       }
-      if (lane < 16) wsum[lane] = xi - x;  // exclusive wave offsets
+      wsum[lane] = xi - x;  // exclusive offsets of (group, wave)
+      if (lane == 63) s_tot = xi;
     }
     __syncthreads();
-    int64_t run = carry + wsum[w] + incl - tot;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = base + 4 * tid + i;
-      run += v[i];
-      if (r < p.n_rows) p.pl_ptr[r + 1] = (int32_t)(run < p.capacity ? run : p.capacity);
+    for (int h = 0; h < kGroups; ++h) {
+      int64_t run = carry + wsum[16 * h + w] + incl[h] - tot[h];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t r = base + 4096 * h + 4 * tid + i;
+        run += v[h][i];
+        if (r < p.n_rows) p.pl_ptr[r + 1] = (int32_t)(run < p.capacity ? run : p.capacity);
+      }
     }
-    if (tid == 1023) s_carry = run;  // the tile's running total
-    __syncthreads();
-    carry = s_carry;
+    carry += s_tot;
+    __syncthreads();  // wsum and s_tot are rewritten by the next tile
   }
   if (tid == 0) {
     p.pl_ptr[0] = 0;
@@ -121,6 +173,54 @@ __global__ void __launch_bounds__(256) plan_fill_kernel(PlanUpdateParams p) {
   }
 }
 
+// entries for plans with few long rows: a 1024-thread workgroup per row, threads over the
+// row's blocks 1024 at a time, placed by a workgroup prefix sum (wave shuffles, then the 16
+// wave totals through LDS)
+__global__ void __launch_bounds__(1024) plan_fill_wide_kernel(PlanUpdateParams p) {
+  __shared__ int wsum[16];
+  __shared__ int s_tot;
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int base = p.pl_ptr[r], end = p.pl_ptr[r + 1];
+  const int j0 = p.row_ptr[r], j1 = p.row_ptr[r + 1];
+  int run = 0;
+  for (int jb = j0; jb < j1; jb += 1024) {
+    const int j = jb + tid;
+    int kb = -1, np = 0;
+    if (j < j1) {
+      kb = p.kblk[j];
+      if (kb >= 0 && kb < p.nkb) np = p.first_page[kb + 1] - p.first_page[kb];
+    }
+    int incl = np;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += v;
+    }
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    if (w == 0) {
+      const int x = lane < 16 ? wsum[lane] : 0;
+      int xi = x;
+#pragma unroll
+      for (int d = 1; d < 16; d <<= 1) {
+        const int y = __shfl_up(xi, d, 64);
+        if (lane >= d) xi += y;
+      }
+      if (lane < 16) wsum[lane] = xi - x;  // exclusive wave offsets
+      if (lane == 15) s_tot = xi;          // pages of these 1024 blocks
+    }
+    __syncthreads();
+    const int pos0 = base + run + wsum[w] + incl - np;
+    for (int i = 0; i < np; ++i) {
+      const int pos = pos0 + i;
+      if (pos < end) p.pl_ent[pos] = p.page_ent[p.first_page[kb] + i];
+    }
+    run += s_tot;
+    __syncthreads();  // wsum and s_tot are rewritten by the next round
+  }
+}
+
 // stage flags: one wave per row, lanes over its 4-entry stages
 __global__ void __launch_bounds__(256) plan_flag_kernel(PlanUpdateParams p) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -128,6 +228,19 @@ __global__ void __launch_bounds__(256) plan_flag_kernel(PlanUpdateParams p) {
   if (r >= p.n_rows) return;
   const int a = p.pl_ptr[r], b = p.pl_ptr[r + 1];
   for (int s0 = a + 4 * lane; s0 < b; s0 += 256) {
+    const int s1 = min(s0 + 4, b);
+    bool partial = s1 - s0 < 4;
+    for (int e = s0; e < s1; ++e) partial |= (p.pl_ent[e] & 31) < 16;
+    if (partial)
+      for (int e = s0; e < s1; ++e) p.pl_ent[e] = (int32_t)((uint32_t)p.pl_ent[e] | 0x80000000u);
+  }
+}
+
+// stage flags for plans with few long rows: a 1024-thread workgroup per row
+__global__ void __launch_bounds__(1024) plan_flag_wide_kernel(PlanUpdateParams p) {
+  const int r = blockIdx.x;
+  const int a = p.pl_ptr[r], b = p.pl_ptr[r + 1];
+  for (int s0 = a + 4 * (int)threadIdx.x; s0 < b; s0 += 4096) {
     const int s1 = min(s0 + 4, b);
     bool partial = s1 - s0 < 4;
     for (int e = s0; e < s1; ++e) partial |= (p.pl_ent[e] & 31) < 16;
@@ -224,10 +337,17 @@ __global__ void __launch_bounds__(256) tpl_fill_kernel(PlanUpdateParams p) {
 
 hipError_t launch_plan_update(const PlanUpdateParams& p, hipStream_t stream) {
   if (p.n_rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(plan_count_kernel, dim3((p.n_rows + 3) / 4), dim3(256), 0, stream, p);
-  hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, stream, p);
-  hipLaunchKernelGGL(plan_fill_kernel, dim3((p.n_rows + 3) / 4), dim3(256), 0, stream, p);
-  hipLaunchKernelGGL(plan_flag_kernel, dim3((p.n_rows + 3) / 4), dim3(256), 0, stream, p);
+  if (p.n_rows < 256) {  // fewer rows than CUs: a workgroup per row
+    hipLaunchKernelGGL(plan_count_wide_kernel, dim3(p.n_rows), dim3(1024), 0, stream, p);
+    hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, stream, p);
+    hipLaunchKernelGGL(plan_fill_wide_kernel, dim3(p.n_rows), dim3(1024), 0, stream, p);
+    hipLaunchKernelGGL(plan_flag_wide_kernel, dim3(p.n_rows), dim3(1024), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(plan_count_kernel, dim3((p.n_rows + 3) / 4), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, stream, p);
+    hipLaunchKernelGGL(plan_fill_kernel, dim3((p.n_rows + 3) / 4), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(plan_flag_kernel, dim3((p.n_rows + 3) / 4), dim3(256), 0, stream, p);
+  }
   const int64_t n_lists = int64_t(p.n_units) * p.nkb;
   if (p.tpl_ptr != nullptr && n_lists > 0) {
     // the transposed lists: count, prefix sum (the same scan, clamped to their capacity), fill

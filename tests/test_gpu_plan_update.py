@@ -43,18 +43,26 @@ def _canonical(w):
     return np.asarray(rp, np.int32), np.asarray(cols, np.int32)
 
 
-@pytest.mark.parametrize("seed,perm,causal,decode", [(401, False, False, False), (402, True, False, False),
-                                                     (403, False, True, False), (404, False, True, True)])
-def test_device_update_equals_host_plan(seed, perm, causal, decode):
+@pytest.mark.parametrize("seed,perm,causal,decode,many_rows", [(401, False, False, False, False),
+                                                               (402, True, False, False, False),
+                                                               (403, False, True, False, False),
+                                                               (404, False, True, True, False),
+                                                               (405, False, False, False, True)])
+def test_device_update_equals_host_plan(seed, perm, causal, decode, many_rows):
+    # the update builds few rows with a workgroup per row and many rows (>= 256, the last case:
+    # ~1,300 rows of small Q blocks) with a wave per row
     if decode:
         w1 = make_chunk_gqa("u1", seed, B=2, Hq=16, Hkv=2, d=128, Nk=64 * 120, Nq=1, chunk=64, topk=30)
         w2 = make_chunk_gqa("u2", seed + 50, B=2, Hq=16, Hkv=2, d=128, Nk=64 * 120, Nq=1, chunk=64, topk=30)
         w2.q, w2.k, w2.v = w1.q, w1.k, w1.v  # same tensors, the second seed's selection
     else:
-        w1 = make_random(seed, B=1, Hq=4, Hkv=2, Nq=400, Nk=600, d=128, max_qblock=130, max_kblock=50, density=0.5,
+        nq, mq = (3000, 8) if many_rows else (400, 130)
+        w1 = make_random(seed, B=1, Hq=4, Hkv=2, Nq=nq, Nk=600, d=128, max_qblock=mq, max_kblock=50, density=0.5,
                          sel_mode="kv", use_perm=perm, causal=causal)
-        w2 = make_random(seed, B=1, Hq=4, Hkv=2, Nq=400, Nk=600, d=128, max_qblock=130, max_kblock=50, density=0.3,
+        w2 = make_random(seed, B=1, Hq=4, Hkv=2, Nq=nq, Nk=600, d=128, max_qblock=mq, max_kblock=50, density=0.3,
                          sel_mode="kv", use_perm=perm, causal=causal)
+        rows = len(w2.sel_row_ptr) - 1
+        assert (rows >= 256) == many_rows, rows
     rp2, kb2 = _canonical(w2)
     a = bs.Plan.from_workload(w1).upload()
     cap = a.stats["page_list_len"]
