@@ -6,7 +6,9 @@
 // short by the row's end carries bit 31 (KPage abstract, zhuanzhiai page 1, sentences 2 and
 // 4).  Four small kernels: page counts per row, a prefix sum into the row pointers (clamped
 // to the entry capacity), the entries, the stage flags; a wave per row, or a workgroup per
-// row when the rows are fewer than the CUs.
+// row when the rows are fewer than the CUs.  Long count arrays are scanned over the whole
+// chip, with the tile totals kept at the start of the entry array until the fill overwrites
+// it (every reader masks entries past a list's end, so what they leave there is never used).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -140,6 +142,124 @@ __global__ void __launch_bounds__(1024) plan_scan_kernel(PlanUpdateParams p) {
   if (tid == 0) {
     p.pl_ptr[0] = 0;
     if (carry > p.capacity) flag(p, 1);
+  }
+}
+
+// The same scan over the whole chip, for count arrays longer than one tile of the kernel
+// above: the totals of 4096-count tiles (plan_tile_sum_kernel), their exclusive scan in one
+// workgroup (plan_tile_scan_kernel), then each tile's own scan from its offset
+// (plan_tile_apply_kernel).  The tile totals live at the start of the entry array, which
+// only the fill writes, after the scan.
+__device__ __forceinline__ int32_t count_at(const PlanUpdateParams& p, int64_t r) {
+  const int32_t x = p.pl_ptr[(r < p.n_rows ? r : p.n_rows - 1) + 1];  // unconditional load
+  return r < p.n_rows ? x : 0;
+}
+
+__global__ void __launch_bounds__(1024) plan_tile_sum_kernel(PlanUpdateParams p, int64_t* tsum) {
+  __shared__ int64_t part[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t base = (int64_t)blockIdx.x * 4096 + 4 * tid;
+  int64_t t = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t += count_at(p, base + i);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) t += __shfl_xor(t, m, 64);
+  if (lane == 0) part[w] = t;
+  __syncthreads();
+  if (tid == 0) {
+    int64_t s = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += part[i];
+    tsum[blockIdx.x] = s;
+  }
+}
+
+__global__ void __launch_bounds__(1024) plan_tile_scan_kernel(int64_t* tsum, int n_tiles) {
+  __shared__ int64_t wsum[16];
+  __shared__ int64_t s_tot;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int64_t carry = 0;
+  for (int base = 0; base < n_tiles; base += 1024) {
+    const int i = base + tid;
+    const int64_t x = i < n_tiles ? tsum[i] : 0;
+    int64_t incl = x;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int64_t y = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += y;
+    }
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    if (w == 0) {
+      const int64_t y = lane < 16 ? wsum[lane] : 0;
+      int64_t yi = y;
+#pragma unroll
+      for (int d = 1; d < 16; d <<= 1) {
+        const int64_t z = __shfl_up(yi, d, 64);
+        if (lane >= d) yi += z;
+      }
+      if (lane < 16) wsum[lane] = yi - y;
+      if (lane == 15) s_tot = yi;
+    }
+    __syncthreads();
+    if (i < n_tiles) tsum[i] = carry + wsum[w] + incl - x;  // exclusive tile offsets
+    carry += s_tot;
+    __syncthreads();
+  }
+}
+
+__global__ void __launch_bounds__(1024) plan_tile_apply_kernel(PlanUpdateParams p, const int64_t* tsum, int n_tiles) {
+  __shared__ int64_t wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t base = (int64_t)blockIdx.x * 4096 + 4 * tid;
+  int32_t v[4];
+  int64_t tot = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = count_at(p, base + i);
+    tot += v[i];
+  }
+  int64_t incl = tot;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t x = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += x;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  if (w == 0) {
+    const int64_t x = lane < 16 ? wsum[lane] : 0;
+    int64_t xi = x;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      const int64_t y = __shfl_up(xi, d, 64);
+      if (lane >= d) xi += y;
+    }
+    if (lane < 16) wsum[lane] = xi - x;
+  }
+  __syncthreads();
+  int64_t run = tsum[blockIdx.x] + wsum[w] + incl - tot;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    run += v[i];
+    if (base + i < p.n_rows) p.pl_ptr[base + i + 1] = (int32_t)(run < p.capacity ? run : p.capacity);
+  }
+  if ((int)blockIdx.x == n_tiles - 1 && tid == 1023 && run > p.capacity) flag(p, 1);  // run: the grand total
+  if (blockIdx.x == 0 && tid == 0) p.pl_ptr[0] = 0;
+}
+
+// prefix sum of p's counts: the chip-wide form when the array spans more than one tile of
+// plan_scan_kernel and the entry array (scratch, capacity entries) holds the tile totals
+static void launch_scan(const PlanUpdateParams& p, int32_t* scratch, int64_t scratch_cap, hipStream_t stream) {
+  const int64_t n_tiles = (int64_t(p.n_rows) + 4095) / 4096;
+  if (p.n_rows > 16384 && (reinterpret_cast<uintptr_t>(scratch) & 7) == 0 && scratch_cap >= 2 * n_tiles) {
+    int64_t* tsum = reinterpret_cast<int64_t*>(scratch);
+    hipLaunchKernelGGL(plan_tile_sum_kernel, dim3((unsigned)n_tiles), dim3(1024), 0, stream, p, tsum);
+    hipLaunchKernelGGL(plan_tile_scan_kernel, dim3(1), dim3(1024), 0, stream, tsum, (int)n_tiles);
+    hipLaunchKernelGGL(plan_tile_apply_kernel, dim3((unsigned)n_tiles), dim3(1024), 0, stream, p,
+                       (const int64_t*)tsum, (int)n_tiles);
+  } else {
+    hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, stream, p);
   }
 }
 
@@ -339,12 +459,12 @@ hipError_t launch_plan_update(const PlanUpdateParams& p, hipStream_t stream) {
   if (p.n_rows <= 0) return hipSuccess;
   if (p.n_rows < 256) {  // fewer rows than CUs: a workgroup per row
     hipLaunchKernelGGL(plan_count_wide_kernel, dim3(p.n_rows), dim3(1024), 0, stream, p);
-    hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, stream, p);
+    launch_scan(p, p.pl_ent, p.capacity, stream);
     hipLaunchKernelGGL(plan_fill_wide_kernel, dim3(p.n_rows), dim3(1024), 0, stream, p);
     hipLaunchKernelGGL(plan_flag_wide_kernel, dim3(p.n_rows), dim3(1024), 0, stream, p);
   } else {
     hipLaunchKernelGGL(plan_count_kernel, dim3((p.n_rows + 3) / 4), dim3(256), 0, stream, p);
-    hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, stream, p);
+    launch_scan(p, p.pl_ent, p.capacity, stream);
     hipLaunchKernelGGL(plan_fill_kernel, dim3((p.n_rows + 3) / 4), dim3(256), 0, stream, p);
     hipLaunchKernelGGL(plan_flag_kernel, dim3((p.n_rows + 3) / 4), dim3(256), 0, stream, p);
   }
@@ -358,12 +478,12 @@ hipError_t launch_plan_update(const PlanUpdateParams& p, hipStream_t stream) {
     if (p.nqb <= 16) {
       const unsigned grid = (unsigned)((n_lists + 255) / 256);
       hipLaunchKernelGGL(tpl_count_small_kernel, dim3(grid), dim3(256), 0, stream, t);
-      hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, stream, t);
+      launch_scan(t, p.tpl_ent, p.tcapacity, stream);
       hipLaunchKernelGGL(tpl_fill_small_kernel, dim3(grid), dim3(256), 0, stream, t);
     } else {
       const unsigned grid = (unsigned)((n_lists + 3) / 4);
       hipLaunchKernelGGL(tpl_count_kernel, dim3(grid), dim3(256), 0, stream, t);
-      hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, stream, t);
+      launch_scan(t, p.tpl_ent, p.tcapacity, stream);
       hipLaunchKernelGGL(tpl_fill_kernel, dim3(grid), dim3(256), 0, stream, t);
     }
   }

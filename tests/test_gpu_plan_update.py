@@ -47,13 +47,16 @@ def _canonical(w):
                                                                (402, True, False, False, False),
                                                                (403, False, True, False, False),
                                                                (404, False, True, True, False),
-                                                               (405, False, False, False, True)])
+                                                               (405, False, False, False, True),
+                                                               (406, False, True, True, True)])
 def test_device_update_equals_host_plan(seed, perm, causal, decode, many_rows):
-    # the update builds few rows with a workgroup per row and many rows (>= 256, the last case:
-    # ~1,300 rows of small Q blocks) with a wave per row
+    # The update builds few rows with a workgroup per row and many rows (>= 256: ~1,300 rows
+    # of small Q blocks) with a wave per row.  Count arrays longer than 16,384 (the decode case
+    # with 5,000 chunks per sequence: 20,000 transposed lists) are scanned over the whole chip.
     if decode:
-        w1 = make_chunk_gqa("u1", seed, B=2, Hq=16, Hkv=2, d=128, Nk=64 * 120, Nq=1, chunk=64, topk=30)
-        w2 = make_chunk_gqa("u2", seed + 50, B=2, Hq=16, Hkv=2, d=128, Nk=64 * 120, Nq=1, chunk=64, topk=30)
+        nch = 5000 if many_rows else 120
+        w1 = make_chunk_gqa("u1", seed, B=2, Hq=16, Hkv=2, d=128, Nk=64 * nch, Nq=1, chunk=64, topk=30)
+        w2 = make_chunk_gqa("u2", seed + 50, B=2, Hq=16, Hkv=2, d=128, Nk=64 * nch, Nq=1, chunk=64, topk=30)
         w2.q, w2.k, w2.v = w1.q, w1.k, w1.v  # same tensors, the second seed's selection
     else:
         nq, mq = (3000, 8) if many_rows else (400, 130)
