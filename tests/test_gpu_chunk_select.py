@@ -48,8 +48,11 @@ def check_unit(summ_gpu, sel_gpu, q, k, chunk, topk, query_index, label):
     _say(f"{label}: summary err {err:.2e}; selection {'equal' if exact else 'equal up to near-ties'}")
 
 
+# chunk counts n: 301, 136, 16, then the sort's edge sizes -- 8192 (the maximum: eight keys
+# per thread), 1025 (padded to 2048: two per thread) and a single short chunk
 @pytest.mark.parametrize("d,Nk,chunk,topk,Hq,Hkv", [(128, 64 * 300 + 17, 64, 120, 8, 2), (64, 5000, 37, 50, 4, 4),
-                                                 (128, 1024, 64, 16, 2, 1)])
+                                                 (128, 1024, 64, 16, 2, 1), (128, 8 * 8192, 8, 3000, 4, 2),
+                                                 (64, 16 * 1025, 16, 1000, 2, 1), (128, 20, 64, 1, 2, 2)])
 def test_chunk_select_small(d, Nk, chunk, topk, Hq, Hkv):
     rng = np.random.default_rng(d + Nk)
     B, Nq = 2, 33
