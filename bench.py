@@ -37,13 +37,17 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 SHORT_NAMES = {1: "tiny3d", 2: "onedim", 3: "videodit3d", 4: "partitions", 5: "chunkgqa"}
 KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_fwd_amd", "csrc", "fwd_kernel.hip")
+DECODE_SRC = os.path.join(ROOT, "block_sparse_attention_fwd_amd", "csrc", "decode_kernel.hip")
+CHUNK_SRC = os.path.join(ROOT, "block_sparse_attention_fwd_amd", "csrc", "chunk_select.hip")
 
 
-def measured_counters(workload):
-    """Per-launch figures recorded by rocprofv3 counter runs in profiles/traffic_<workload>.txt
-    (key = value lines), or {} unless the kernel source is the one measured."""
+def measured_counters(workload, name=None, src=KERNEL_SRC):
+    """Per-launch figures recorded by rocprofv3 counter runs in profiles/traffic_<name>.txt
+    (key = value lines; name defaults to the workload's short name), or {} unless the kernel
+    source src is the one measured."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"traffic_{SHORT_NAMES.get(workload, '')}.txt")
+    name = name or SHORT_NAMES.get(workload, "")
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.txt")
     if not os.path.exists(path):
         return {}
     kv = {}
@@ -51,8 +55,18 @@ def measured_counters(workload):
         if "=" in line and not line.lstrip().startswith("#"):
             key, val = line.split("=", 1)
             kv[key.strip()] = val.strip()
-    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     return kv if kv.get("source_sha256") == sha else {}
+
+
+def measured_bytes(name, src, tags):
+    """HBM bytes per call (read + write, summed over the kernels tagged) from the counter runs
+    in profiles/traffic_<name>.txt, or None unless src is the source measured."""
+    kv = measured_counters(None, name, src)
+    try:
+        return sum(int(kv[f"{t}.read_bytes"]) + int(kv[f"{t}.write_bytes"]) for t in tags)
+    except KeyError:
+        return None
 
 
 def measured_traffic(workload, shape_tag):
@@ -221,7 +235,8 @@ def bench_chunk_select(args, w, dev):
         "config": {"workload": w.name, "pass": "chunk selection", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq,
                    "Nk": w.Nk, "d": w.d, "chunk": chunk, "topk": topk, "n_chunks": n, "bytes": nbytes},
         "roofline": {"bound": "hbm", "achieved": round(nbytes / (ev_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(nbytes / (ev_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(nbytes / (ev_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "traffic": measured_bytes("chunkselect", CHUNK_SRC, ("chunk_summary_kernel", "chunk_topk_kernel")),
                      "kernel": f"chunk_summary_kernel<{w.d}> + chunk_topk_kernel<{w.d}>", "kernel_ms": round(ev_ms, 4)},
         "cpu_baseline": None,
     }
@@ -304,7 +319,8 @@ def bench_decode(args, dev):
                    "speedup_over_plain_forward": round(ms_fwd / ms_dec, 2),
                    "device_step_ms": round(ms_pipe, 4)},
         "roofline": {"bound": "hbm", "achieved": round(nbytes / (ev_dec * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(nbytes / (ev_dec * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(nbytes / (ev_dec * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "traffic": measured_bytes("decode", DECODE_SRC, ("fwd_decode_kernel", "decode_merge_kernel")),
                      "kernel": "fwd_decode_kernel<128> + decode_merge_kernel<128>", "kernel_ms": round(ev_dec, 4)},
         "cpu_baseline": None,
     }
