@@ -38,6 +38,25 @@ def test_hand_worked_plan():
     assert [list(x) for x in zip(p.qt_qblock, p.qt_row0, p.qt_rows, p.qt_shape)] == e["qtiles"]
     assert [p.pl_pages[p.pl_ptr[i]:p.pl_ptr[i + 1]].tolist() for i in range(len(p.pl_ptr) - 1)] == e["page_lists"]
     assert (p.physical, p.useful, p.n_ktiles) == (e["physical"], e["useful"], e["n_ktiles"])
+    assert p.useful_by_shape == tuple(e["useful_by_shape"])
+    assert p.physical_by_shape == tuple(e["physical_by_shape"])
+
+
+def test_hand_worked_plan_causal():
+    """The same hand-worked layout under a causal mask with a negative query offset: the
+    useful pairs of each tile shape counted by hand; the plan itself does not change."""
+    g = _load("plan_hand.json")
+    c = g["causal"]
+    qo = np.concatenate([[0], np.cumsum(g["q_block_sizes"])]).astype(np.int32)
+    ko = np.concatenate([[0], np.cumsum(g["k_block_sizes"])]).astype(np.int32)
+    rp = np.concatenate([[0], np.cumsum([len(r) for r in g["selection"]])]).astype(np.int32)
+    cols = np.array([x for r in g["selection"] for x in r], dtype=np.int32)
+    p = build_plan(1, 1, 1, qo, None, ko, None, 1, 1, rp, cols, causal=True, q_pos0=c["q_pos0"])
+    e = g["expect"]
+    assert [p.pl_pages[p.pl_ptr[i]:p.pl_ptr[i + 1]].tolist() for i in range(len(p.pl_ptr) - 1)] == e["page_lists"]
+    assert p.useful == c["useful"]
+    assert p.useful_by_shape == tuple(c["useful_by_shape"])
+    assert p.physical_by_shape == tuple(c["physical_by_shape"])
 
 
 def _axis_pairs(sizes, r):
@@ -62,6 +81,24 @@ def test_box_mask_counts_closed_form(cfg, key):
     assert p.physical == g["physical_per_head"] * g["heads"]
     if "qtiles128" in g:
         assert (p.n_qtiles128, p.n_qtiles64) == (g["qtiles128"], g["qtiles64"])
+    # split by the shape of the Q tile holding the query: the routing (R4) sends a cube to
+    # the 64-row shape iff it holds at most 64 tokens; with cube extents s_a(i) per axis,
+    # the useful pairs of the cubes of either kind follow from the same per-axis sums
+    sizes = [_axis_sizes(n, c) for n, c in zip(g["grid"], g["cube"])]
+    cube_sizes = {}
+    for i in range(len(sizes[0])):
+        for j in range(len(sizes[1])):
+            for k in range(len(sizes[2])):
+                cube_sizes[(i, j, k)] = sizes[0][i] * sizes[1][j] * sizes[2][k]
+    rad = g["radius"]
+    split = [0, 0]
+    for qc, n in cube_sizes.items():
+        row = [sum(sizes[a][j] for j in range(len(sizes[a])) if abs(j - qc[a]) <= rad[a]) for a in range(3)]
+        split[1 if n <= 64 else 0] += n * row[0] * row[1] * row[2]
+    split = [x * g["heads"] for x in split]
+    assert split == g["useful_by_shape"]
+    assert p.useful_by_shape == tuple(g["useful_by_shape"])
+    assert p.physical_by_shape == tuple(x * g["heads"] for x in g["physical_by_shape_per_head"])
 
 
 def test_onedim_exact_density():
@@ -109,13 +146,15 @@ def _graph_pairs(w, b, h):
          causal=True, allow_empty=True),
     dict(seed=64, Hq=1, Hkv=1, Nq=333, Nk=280, max_qblock=70, max_kblock=20, sel_mode="shared",
          allow_empty=True, unsorted=True, dup=True, density=0.7),
+    dict(seed=66, Hq=2, Hkv=1, Nq=280, Nk=300, max_qblock=110, max_kblock=50, sel_mode="kv", causal=True,
+         use_perm=True, allow_empty=True),
 ])
 def test_tiles_cover_graph_exactly(kw):
     w = make_random(d=8, with_tensors=False, **kw)
     p = build_plan_w(w)
     nqb = len(w.q_offsets) - 1
-    cells = 0
-    useful = 0
+    cells = [0, 0]
+    useful = [0, 0]
     for b in range(w.B):
         for h in range(w.Hq):
             g = h // (w.Hq // w.Hkv)
@@ -124,12 +163,13 @@ def test_tiles_cover_graph_exactly(kw):
             seen = []
             for t in range(len(p.qt_qblock)):
                 shape = int(p.qt_shape[t])
+                assert shape == (1 if int(p.qt_rows[t]) <= 64 else 0)
                 row = unit * nqb + int(p.qt_qblock[t])
                 pages = p.pl_pages[p.pl_ptr[row]:p.pl_ptr[row + 1]]
                 ppt = PAGES_PER_KTILE[shape]
                 for k0 in range(0, len(pages), ppt):
                     tile_pages = list(pages[k0:k0 + ppt])
-                    cells += TILE_ROWS[shape] * TILE_COLS[shape]
+                    cells[shape] += TILE_ROWS[shape] * TILE_COLS[shape]
                     for r in range(int(p.qt_rows[t])):
                         i = _slot_token(w.q_perm, int(p.qt_row0[t]) + r)
                         for pg in tile_pages:
@@ -137,11 +177,14 @@ def test_tiles_cover_graph_exactly(kw):
                                 j = _slot_token(w.k_perm, int(p.page_slot0[pg]) + c)
                                 if not w.causal or j <= w.q_pos0 + i:
                                     seen.append((i, j))
+                                    useful[shape] += 1
             assert len(seen) == len(set(seen)), "a pair is covered twice"
             assert set(seen) == _graph_pairs(w, b, h)
-            useful += len(seen)
-    assert cells == p.physical
-    assert useful == p.useful
+    assert sum(cells) == p.physical
+    assert sum(useful) == p.useful
+    # the split by the shape of the tile that holds the query, cell by cell
+    assert tuple(cells) == p.physical_by_shape
+    assert tuple(useful) == p.useful_by_shape
     assert p.n_ktiles * 16384 == p.physical
 
 
@@ -174,7 +217,7 @@ def test_cube_physical_independent_derivation():
     st, sh, sw = _axis_sizes(21, 2), _axis_sizes(45, 8), _axis_sizes(80, 8)
     cubes = [(a, b, c) for a in range(len(st)) for b in range(len(sh)) for c in range(len(sw))]
     size = {x: st[x[0]] * sh[x[1]] * sw[x[2]] for x in cubes}
-    phys = 0
+    phys = {128: 0, 256: 0}
     for qc in cubes:
         pages = sum(-(-size[kc] // 16) for kc in cubes
                     if abs(kc[0] - qc[0]) <= 1 and abs(kc[1] - qc[1]) <= 2 and abs(kc[2] - qc[2]) <= 2)
@@ -182,8 +225,11 @@ def test_cube_physical_independent_derivation():
         tiles = [128] * (n // 128) + ([64] if 0 < n % 128 <= 64 else [128] if n % 128 else [])
         for rows in tiles:
             width = 128 if rows == 128 else 256
-            phys += rows * width * -(-pages // (width // 16))
-    assert phys == build_plan_w(w).physical == 485621760
+            phys[width] += rows * width * -(-pages // (width // 16))
+    p = build_plan_w(w)
+    assert phys[128] + phys[256] == p.physical == 485621760
+    # split by tile width: 128-key tiles belong to the 128-row shape, 256-key tiles to the 64-row one
+    assert (phys[128], phys[256]) == p.physical_by_shape == (472940544, 12681216)
 
 
 # ---------------------------------------------------------------------------
