@@ -12,6 +12,7 @@
 
 namespace bsattn {
 hipError_t launch_fwd_shape(const FwdParams& p, int shape, int d, hipStream_t stream);
+hipError_t launch_fwd(const FwdParams& p, int d, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, int d, hipStream_t stream);
 hipError_t launch_chunk_select(const ChunkParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t stream);
@@ -215,6 +216,19 @@ int run_fwd(const bsattn_plan* plan, int sh0, int sh1, const void* q, const void
   for (int sh = sh0; sh < sh1; ++sh) {
     const int64_t nw = int64_t(plan->n_qt[sh]) * bh;
     if (nw >= (int64_t(1) << 31)) return BSATTN_E_UNSUPPORTED;
+  }
+  if (int64_t(plan->n_qt[0]) * bh + int64_t(plan->n_qt[1]) * bh >= (int64_t(1) << 31)) return BSATTN_E_UNSUPPORTED;
+  if (sh0 == 0 && sh1 == bsattn::kShapes) {
+    // both shapes: one launch where the kernels allow it
+    fp.qtiles = reinterpret_cast<const bsattn::QTileDev*>(base + plan->off_qt[0]);
+    fp.n_qtiles = plan->n_qt[0];
+    fp.n_work = int32_t(int64_t(plan->n_qt[0]) * bh);
+    fp.qtiles2 = reinterpret_cast<const bsattn::QTileDev*>(base + plan->off_qt[1]);
+    fp.n_qtiles2 = plan->n_qt[1];
+    fp.n_work2 = int32_t(int64_t(plan->n_qt[1]) * bh);
+    hipError_t e = bsattn::launch_fwd(fp, pr.d, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e);
+    return BSATTN_OK;
   }
   for (int sh = sh0; sh < sh1; ++sh) {
     bsattn::FwdParams f = fp;

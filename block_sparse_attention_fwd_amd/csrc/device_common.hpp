@@ -110,5 +110,10 @@ __device__ __forceinline__ float sum16(const float* x) {
   const float c = (x[8] + x[9]) + (x[10] + x[11]), d = (x[12] + x[13]) + (x[14] + x[15]);
   return (a + b2) + (c + d);
 }
+__device__ __forceinline__ float sum16v(const f32x16& x) {
+  const float a = (x[0] + x[1]) + (x[2] + x[3]), b2 = (x[4] + x[5]) + (x[6] + x[7]);
+  const float c = (x[8] + x[9]) + (x[10] + x[11]), d = (x[12] + x[13]) + (x[14] + x[15]);
+  return (a + b2) + (c + d);
+}
 
 }  // namespace bsattn

@@ -1,16 +1,16 @@
 // Exact block-sparse attention forward for gfx950 (MI355X).
 //
-// One workgroup (4 waves) owns one Q tile of one (batch, head) and walks its K tiles.
-// A K tile is 8 or 16 page-list entries; each entry is a 16-row K/V page of one block,
-// so a tile packs pages of several logical blocks (KPage abstract, zhuanzhiai page 1,
-// sentence 2).  Pages are gathered from HBM straight into LDS (global_load_lds, 16 bytes
-// per lane): nothing compacted is ever written back.  Q tiles come in two shapes
-// (sentence 3): 128 rows x 128 keys (4 row groups of 32 queries, one per wave) and 64 rows
-// x 256 keys (2 row groups x 2 key groups; the key groups keep separate softmax states
-// that are merged at the end).  Exact masking (sentence 4) clears empty page slots and,
-// for causal problems, keys after the query.
+// A Q tile of one (batch, head) walks its page list: every entry is a 16-row K/V page of
+// one block, so the stages loaded into LDS pack pages of several logical blocks (KPage
+// abstract, zhuanzhiai page 1, sentence 2).  Pages are gathered from HBM straight into LDS
+// (global_load_lds, 16 bytes per lane): nothing compacted is ever written back.  Q tiles
+// come in two shapes (sentence 3): 128 rows x 128-key K tiles and 64 rows x 256-key K
+// tiles.  Exact masking (sentence 4) clears empty page slots and, for causal problems, keys
+// after the query.
 //
-// Per wave and K tile the work is 32 queries x 128 keys:
+// The main path is the ping-pong walk further down (both shapes, one launch).  The 4-wave
+// kernel right below serves the problems the walk does not take (permuted keys under a
+// causal mask): per wave and K tile it does 32 queries x 64 keys --
 //   S^T = K Q^T    v_mfma_f32_32x32x16_bf16, A = K rows from LDS, B = Q^T in registers;
 //                  the accumulator gives each lane one query (lane % 32) and 64 keys.
 //   online softmax in fp32 (row max / sum per lane, one cross-half exchange),
@@ -22,6 +22,7 @@
 // matrix cores work while the next block's exponentials are computed.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "device_common.hpp"
@@ -42,16 +43,10 @@ struct Cfg {
   static constexpr int kBufBytes = kTileK * kRowBytes;
   static constexpr int kDS = D / 16;                 // k-steps of QK^T
   static constexpr int kDB = D / 32;                 // 32-wide d blocks of O^T
-  // two workgroups per CU when the LDS allows it
-  // workgroups per CU that the LDS allows (at most 3: the register budget of 168)
+  // two workgroups per CU when the LDS allows it (three waves per SIMD would leave 168
+  // VGPRs: too few)
   static constexpr int kLds = 2 * kBufBytes + kTileK * 4;
-#ifdef BSATTN_WPE_MAX
-  static constexpr int kWpeMax = BSATTN_WPE_MAX;
-#else
-  static constexpr int kWpeMax = 2;  // three waves per SIMD would leave 168 VGPRs: too few
-#endif
-  static constexpr int kWavesPerEU =
-      (kWpeMax >= 3 && 3 * kLds <= 160 * 1024) ? 3 : ((kWpeMax >= 2 && 2 * kLds <= 160 * 1024) ? 2 : 1);
+  static constexpr int kWavesPerEU = 2 * kLds <= 160 * 1024 ? 2 : 1;
 };
 
 template <int D, int NRG, int NKG, int KB, bool KPERM>
@@ -406,19 +401,30 @@ __global__ void __launch_bounds__(256)
 }
 
 // ---------------------------------------------------------------------------------------
-// 128x128 tiles in ping-pong: 8 waves, two per SIMD.  Waves 0-3 (group 0) and 4-7 (group 1)
-// each hold the tile's four row groups of 32 queries and split its 64-key stages (4 pages):
-// group g takes stages g, g + 2, g + 4, ...  The walk alternates two kinds of phase between
-// workgroup barriers: a matrix phase (P.V of the group's previous stage, then S^T = K Q^T of
-// its current one: 32 MFMAs per wave at d = 128) and a vector phase (mask, online softmax
-// and exponentials of the current stage, plus transposing the stage's V into ready-made
-// MFMA operands in LDS).  Group 1 runs one phase behind group 0, so in every phase each SIMD
-// holds one wave issuing MFMAs and one issuing vector instructions, and the two execute side
-// by side.  Staging V^T moves the transposing LDS reads out of the matrix phase, whose every
-// operand is then a single 16-byte read (a wave can only keep a few LDS reads in flight, so
-// their count bounds the matrix phase).  Each group keeps its own softmax state over its
-// stages; the two are merged at the end.  K and V stages are double-buffered per group and
-// loaded two to three phases before they are read.
+// Ping-pong walk: 8 waves, two per SIMD.  Waves 0-3 (group 0) and 4-7 (group 1) split the
+// tile's 64-key stages (4 pages): group g takes stages g, g + 2, g + 4, ...  The walk
+// alternates two kinds of phase between workgroup barriers: a matrix phase (P.V of the
+// group's previous stage, then S^T = K Q^T of its current one) and a vector phase (mask,
+// online softmax and exponentials of the current stage, plus transposing the stage's V into
+// ready-made MFMA operands in LDS).  Group 1 runs one phase behind group 0, so in every phase
+// each SIMD holds one wave issuing MFMAs and one issuing vector instructions, and the two
+// execute side by side.  Staging V^T moves the transposing LDS reads out of the matrix phase,
+// whose every operand is then a single 16-byte read (a wave can only keep a few LDS reads in
+// flight, so their count bounds the matrix phase).  K and V stages are double-buffered per
+// group and loaded two to three phases before they are read.
+//
+// The two Q-tile shapes of the plan (KPage abstract, zhuanzhiai page 1, sentence 3) differ
+// only in how a group's four waves share a stage:
+//   128-row tiles: wave w of a group holds row group w (32 queries) and all 64 keys of the
+//                  stage (two 32-key blocks): 32 MFMAs per wave and matrix phase at d = 128;
+//   64-row tiles:  wave w holds row group w & 1 and the 32-key half w >> 1 of the stage:
+//                  16 MFMAs per matrix phase.  Four consecutive stages are one 256-key K
+//                  tile of the plan; two groups x two slots keep all four in LDS at once.
+// Each (group, key half) keeps its own softmax state over its keys; the states of a row
+// group are merged through LDS at the end.  In a 64-row tile of at most 32 valid rows, the
+// waves of the second row group skip their products and exponentials but keep their share
+// of the loads, the V transposition and every barrier.  Both shapes use the same LDS stage
+// layout, so one launch can run tiles of both kinds.
 //
 // The softmax reference max is lazy: it moves only when a stage's max exceeds it by more
 // than 2^8 in exp2 units, so O is rescaled a few times per tile instead of at most stages.
@@ -433,45 +439,54 @@ struct PPCfg {
   static constexpr int kStage = 64 * kRowBytes;       // one 64-key stage of K or V
   static constexpr int kDS = D / 16;                  // k-steps of QK^T
   static constexpr int kDB = D / 32;                  // 32-wide d blocks of O^T
+  // a wave's end state for the merge: O^T accumulators (kDB x 16 floats per lane)
+  static constexpr int kRecord = kDB * 16 * 64 * 4;
 };
 
 constexpr float kLazySlack = 8.f;  // log2 units the reference max may trail the true max
 
-template <int D, bool KPERM>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) fwd_kernel_pp(FwdParams p) {
+// LDS of the walk: stage buffers by slot (group g's stage at offset g * kStage of each
+// array) and the V^T operands of each group's current stage.  Five separate objects, so the
+// compiler can tell reads of one from loads into another.
+template <int D>
+struct PPSmem {
+  uint8_t* sk0;
+  uint8_t* sk1;
+  uint8_t* sv0;
+  uint8_t* sv1;
+  uint8_t* svt;
+};
+
+// One Q tile (work item `work` of the tiles at qtiles) walked by the workgroup.  R64: the
+// tile is a 64-row tile (see above).
+template <int D, bool KPERM, bool R64>
+__device__ __forceinline__ void pp_walk(const FwdParams& p, const CONST_AS int32_t* qtiles, int n_qtiles, int work,
+                                        const PPSmem<D>& sm) {
   using C = PPCfg<D>;
-  // Stage buffers by slot; group g's stage sits at offset g * kStage of each array.  Four
-  // separate objects, so the compiler can tell reads of one slot from loads into another.
-  __shared__ __attribute__((aligned(1024))) uint8_t sk0[2 * C::kStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t sk1[2 * C::kStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t sv0[2 * C::kStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t sv1[2 * C::kStage];
-  // V^T of each group's current stage as ready-made MFMA operands (operand o: 64 lanes x 16 B)
-  __shared__ __attribute__((aligned(1024))) uint8_t svt[2 * C::kStage];
-  static_assert((C::kDB * 16 + 2) * 64 * 4 <= 2 * C::kStage, "merge buffer fits");
+  constexpr int JB = R64 ? 1 : 2;  // 32-key blocks of a stage per wave
+  uint8_t* const sk0 = sm.sk0;
+  uint8_t* const sk1 = sm.sk1;
+  uint8_t* const sv0 = sm.sv0;
+  uint8_t* const sv1 = sm.sv1;
+  uint8_t* const svt = sm.svt;
   static_assert(4 * C::kDB * 1024 == C::kStage, "one 1 KB operand per 16 keys x 32 d");
+  static_assert(2 * C::kRecord <= 2 * C::kStage && 6 * 2 * 64 * 4 <= 2 * C::kStage, "merge records fit");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2;  // stage group
-  const int wr = wave & 3;    // row group, and the page of each stage this wave loads
+  const int grp = wave >> 2;                  // stage group
+  const int wr = wave & 3;                    // the page of each stage this wave loads and transposes
+  const int rg = R64 ? (wr & 1) : wr;         // row group
+  const int kh = R64 ? (wr >> 1) : 0;         // key half of the stage (64-row tiles)
   const int hh = lane >> 5;
 
   const CONST_AS int32_t* pl_ent = (const CONST_AS int32_t*)p.pl_ent;
   const CONST_AS int32_t* pl_ptr = (const CONST_AS int32_t*)p.pl_ptr;
-  const CONST_AS int32_t* qtiles = (const CONST_AS int32_t*)p.qtiles;
   const CONST_AS int32_t* kperm = (const CONST_AS int32_t*)p.kperm;
 
-  // ---- work item (XCD-aware: consecutive items share an XCD's L2) ----
-  int work;
-  {
-    const int n = p.n_work, blk = blockIdx.x;
-    const int x = blk & 7, i = blk >> 3, q = n >> 3, r = n & 7;
-    work = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
-  }
-  const int bh = work / p.n_qtiles;
-  const int t = work - bh * p.n_qtiles;
+  const int bh = work / n_qtiles;
+  const int t = work - bh * n_qtiles;
   const int b = bh / p.Hq;
   const int h = bh - b * p.Hq;
   const int g = h / p.grp;
@@ -482,9 +497,13 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int e1 = pl_ptr[row + 1];
   const int ns = (e1 - e0 + 3) >> 2;        // 64-key stages
   const int my_n = (ns + 1 - grp) >> 1;     // this group's stages: global 2j + grp, j < my_n
+  // A row group of a 64-row tile past the tile's valid rows holds only padding: no products
+  // for it (uniform).  The 128-row tiles keep every row group busy: skipping there measured
+  // slower on the video-DiT layout (its code then branches in every phase).
+  const bool active = R64 ? rg * 32 < qt_rows : true;
 
   // ---- Q^T operand: lane holds query (lane % 32) of its row group, 8 d per k-step ----
-  const int qrow = wr * 32 + (lane & 31);
+  const int qrow = rg * 32 + (lane & 31);
   const bool qvalid = qrow < qt_rows;
   const int qslot = qt_row0 + (qvalid ? qrow : 0);
   const int qtok = p.qperm ? p.qperm[qslot] : qslot;
@@ -500,7 +519,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int64_t qp = p.q_pos0 + (int64_t)qtok;
     thr = qp < -1 ? -1 : (qp > 0x7ffffffe ? 0x7ffffffe : (int)qp);
   }
-  const int64_t minq_pos = p.q_pos0 + qt_row0 + wr * 32;  // smallest query position of the wave (identity Q)
+  const int64_t minq_pos = p.q_pos0 + qt_row0 + rg * 32;  // smallest query position of the wave (identity Q)
 
   // ---- loader: page wr of a stage -> rows wr * 16 .. + 15 of the group's stage buffer ----
   const int ld_lr = lane / C::kChunks;
@@ -585,13 +604,13 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int n = 0; n < C::kInst; ++n) fire(L, rsrc, buf, n);
   };
 
-  // ---- per-wave state: softmax of the group's stages, O^T, P of the last stage ----
+  // ---- per-wave state: softmax of the wave's keys, O^T, P of the last stage ----
   float mref = kNegInf;  // reference max, scaled to exp2 units
   float l_run = 0.f;
   f32x16 oacc[C::kDB];
 #pragma unroll
   for (int db = 0; db < C::kDB; ++db) oacc[db] = f32x16{};
-  f32x16 sacc[2];  // S^T of the stage; after the vector phase, its P (fp32) until the next P.V
+  f32x16 sacc[JB];  // S^T of the stage; after the vector phase, its P (fp32) until the next P.V
   const float sl2 = p.scale_log2;
 
   int nbar = 0;
@@ -604,14 +623,15 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   // Per-lane LDS byte offsets inside the group's stage, so that slot arrays, key blocks and
   // 16-key chunks all become immediate offsets of a few address registers.  K operand of
-  // k-step s: row lane % 32 (+ 32 per key block), logical chunk 2s + hh.  V^T operand of d
-  // block db: transposed reads of keys 4hh + v_rr and 4hh + v_rr + 8 (+ 16 per chunk).  A
-  // row's swizzle depends only on its low four bits, which the block and chunk steps keep.
+  // k-step s: row 32 kh + lane % 32 (+ 32 per key block), logical chunk 2s + hh.  V^T operand
+  // of d block db: transposed reads of keys 4hh + v_rr and 4hh + v_rr + 8 (+ 16 per chunk).
+  // A row's swizzle depends only on its low four bits, which the block and chunk steps keep.
   uint32_t kofs[C::kDS], vofa[C::kDB], vofb[C::kDB];
   {
     const int r = lane & 31;
 #pragma unroll
-    for (int s = 0; s < C::kDS; ++s) kofs[s] = goff + r * C::kRowBytes + (((2 * s + hh) ^ swz<D>(r)) * 16);
+    for (int s = 0; s < C::kDS; ++s)
+      kofs[s] = goff + (32 * kh + r) * C::kRowBytes + (((2 * s + hh) ^ swz<D>(r)) * 16);
     const int v_rr = (lane & 15) >> 2, v_qq = lane & 3, v_dsub = (lane >> 4) & 1;
     const int key_a = 4 * hh + v_rr, key_b = key_a + 8;
 #pragma unroll
@@ -627,64 +647,73 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   // V^T operands (chunk wr, d block db) of the next matrix phase, each stored as 64 lanes x
   // 16 bytes, so that phase reads every operand with one conflict-free 16-byte load.
   const uint32_t opofs = goff + lane * 16;
+  // first V^T operand of this wave's keys: chunks 2 kh, 2 kh + 1 of a 64-row tile's stage
+  const uint32_t vtofs = opofs + 2 * kh * C::kDB * 1024;
   struct VtOps {
     bf16x8 op[C::kDB];
   };
   auto transpose_read = [&](const uint8_t* vb) __attribute__((always_inline)) {
-    VtOps t;
+    VtOps tv;
 #pragma unroll
     for (int db = 0; db < C::kDB; ++db) {
       const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(vb + vofa[db] + wr * 16 * C::kRowBytes));
       const bf16x4 vq = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(vb + vofb[db] + wr * 16 * C::kRowBytes));
-      t.op[db] = bf16x8{va[0], va[1], va[2], va[3], vq[0], vq[1], vq[2], vq[3]};
+      tv.op[db] = bf16x8{va[0], va[1], va[2], va[3], vq[0], vq[1], vq[2], vq[3]};
     }
-    return t;
+    return tv;
   };
-  auto transpose_write = [&](const VtOps& t) __attribute__((always_inline)) {
+  auto transpose_write = [&](const VtOps& tv) __attribute__((always_inline)) {
 #pragma unroll
-    for (int db = 0; db < C::kDB; ++db) *reinterpret_cast<bf16x8*>(svt + opofs + (wr * C::kDB + db) * 1024) = t.op[db];
+    for (int db = 0; db < C::kDB; ++db) *reinterpret_cast<bf16x8*>(svt + opofs + (wr * C::kDB + db) * 1024) = tv.op[db];
   };
 
   // Matrix phase: O^T += V^T P^T over the staged V^T operands (PV), then S^T = K Q^T over the
   // K stage at kb (QK).  The products run as one list (PV: 16-key chunk c, d block db; QK:
   // k-step s, key block j) whose operands are read kLead products ahead of their use, so
-  // the matrix core does not stall on LDS latency between products.
-  constexpr int kNPV = 4 * C::kDB, kNQK = 2 * C::kDS, kLead = 4;
+  // the matrix core does not stall on LDS latency between products.  A wave without valid
+  // rows issues only the loads.
+  constexpr int kNPV = 2 * JB * C::kDB, kNQK = JB * C::kDS, kLead = 4;
   auto mphase = [&](const uint8_t* kb, auto pv_tag, auto qk_tag, const PageLoad* ldk, uint8_t* kdst, const PageLoad* ldv,
                     uint8_t* vdst) __attribute__((always_inline)) {
     constexpr bool PV = decltype(pv_tag)::value, QK = decltype(qk_tag)::value;
     constexpr int n0 = PV ? 0 : kNPV;
     constexpr int n1 = QK ? kNPV + kNQK : kNPV;
     constexpr int kSpread = (n1 - n0) / (2 * C::kInst);  // one load before every kSpread-th product
+    static_assert(kSpread >= 1, "a product per load");
+    if (!active) {
+      if (ldk) {
+#pragma unroll
+        for (int n = 0; n < C::kInst; ++n) fire(*ldk, krsrc, kdst, n);
+#pragma unroll
+        for (int n = 0; n < C::kInst; ++n) fire(*ldv, vrsrc, vdst, n);
+      }
+      return;
+    }
     // The SIMD's arbiter favours older waves; raising the matrix wave's priority keeps its
     // MFMAs flowing whichever group is in the vector phase.
     __builtin_amdgcn_s_setprio(2);
     // P of the previous stage (fp32 in sacc) as bf16 operands, and its row sum: vector work
-    // that this wave's idle VALU slots absorb while its MFMAs run
-    bf16x8 pbuf[4];
+    // that this wave's idle VALU slots absorb while its MFMAs run.  The sum is taken over the
+    // fp32 probabilities: with bf16 ones a row of few keys would carry up to 2^-9 relative
+    // error into its log-sum-exp.
+    bf16x8 pbuf[2 * JB];
     if constexpr (PV) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb2 = 0; kb2 < JB; ++kb2)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) pbuf[2 * kb + (e >> 3)][e & 7] = (__bf16)sacc[kb][e];
-      // row sum of the bf16 probabilities (the ones P.V uses): two at a time with v_dot2
-      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-      const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
-      float ls[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int e = 0; e < 8; e += 2)
-          ls[c] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pbuf[c][e], pbuf[c][e + 1]}, one2, ls[c], false);
-      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        for (int e = 0; e < 16; ++e) pbuf[2 * kb2 + (e >> 3)][e & 7] = (__bf16)sacc[kb2][e];
+      if constexpr (JB == 2)
+        l_run += sum16v(sacc[0]) + sum16v(sacc[1]);
+      else
+        l_run += sum16v(sacc[0]);
     }
     bf16x8 ring[kLead + 1];
     auto load = [&](auto it) __attribute__((always_inline)) {
       constexpr int i = decltype(it)::value;
       if constexpr (i < kNPV) {
-        ring[(i - n0) % (kLead + 1)] = *reinterpret_cast<const bf16x8*>(svt + opofs + i * 1024);
+        ring[(i - n0) % (kLead + 1)] = *reinterpret_cast<const bf16x8*>(svt + vtofs + i * 1024);
       } else {
-        constexpr int s = (i - kNPV) / 2, j = (i - kNPV) % 2;
+        constexpr int s = (i - kNPV) / JB, j = (i - kNPV) % JB;
         ring[(i - n0) % (kLead + 1)] = *reinterpret_cast<const bf16x8*>(kb + kofs[s] + j * 32 * C::kRowBytes);
       }
     };
@@ -695,7 +724,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
         constexpr int c = i / C::kDB, db = i % C::kDB;
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pbuf[c], oacc[db], 0, 0, 0);
       } else {
-        constexpr int s = (i - kNPV) / 2, j = (i - kNPV) % 2;
+        constexpr int s = (i - kNPV) / JB, j = (i - kNPV) % JB;
         sacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], s == 0 ? f32x16{} : sacc[j], 0, 0, 0);
       }
     };
@@ -703,11 +732,11 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     static_for<n0, n1>([&](auto it) __attribute__((always_inline)) {
       constexpr int i = decltype(it)::value;
       if constexpr ((i - n0) % kSpread == 0) {
-        constexpr int t = (i - n0) / kSpread;
-        if constexpr (t < C::kInst) {
-          if (ldk) fire(*ldk, krsrc, kdst, t);
-        } else if constexpr (t < 2 * C::kInst) {
-          if (ldv) fire(*ldv, vrsrc, vdst, t - C::kInst);
+        constexpr int tt = (i - n0) / kSpread;
+        if constexpr (tt < C::kInst) {
+          if (ldk) fire(*ldk, krsrc, kdst, tt);
+        } else if constexpr (tt < 2 * C::kInst) {
+          if (ldv) fire(*ldv, vrsrc, vdst, tt - C::kInst);
         }
       }
       if constexpr (i + kLead < n1) load(IntTag<i + kLead>{});
@@ -724,8 +753,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     });
     // the products stay in this phase (see pin_vector_phase)
-    pin(sacc[0]);
-    pin(sacc[1]);
+#pragma unroll
+    for (int j = 0; j < JB; ++j) pin(sacc[j]);
     pin(l_run);
 #pragma unroll
     for (int db = 0; db < C::kDB; ++db) pin(oacc[db]);
@@ -737,8 +766,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   // matrix phase's MFMAs (and could hoist matrix work the other way), so the results of each
   // phase are tied to its end by empty asm statements that use them.
   auto pin_vector_phase = [&]() __attribute__((always_inline)) {
-    pin(sacc[0]);
-    pin(sacc[1]);
+#pragma unroll
+    for (int j = 0; j < JB; ++j) pin(sacc[j]);
     pin(l_run);
     pin(mref);
 #pragma unroll
@@ -747,7 +776,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   // Mask, online softmax and P (in place, fp32) of a stage with page entries ev (S^T in sacc);
   // its row sum and bf16 conversion happen in the next matrix phase.
-  auto softmax = [&](const SVec<4>& raw, int j, auto&& at) __attribute__((always_inline)) {
+  auto softmax = [&](const SVec<4>& raw, int j) __attribute__((always_inline)) {
     // the planner flags stages with a partial page or a cut-short end (bit 31 of the first
     // entry); causal problems also mask stages whose keys may follow a query
     bool need = raw[0] < 0;
@@ -764,25 +793,32 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     if (need) {
       const SVec<4> ev = valid(raw, j);
-      int ment[4];
+      // entries of this wave's pages: 2 (kb + kh) and 2 (kb + kh) + 1 for key block kb
+      int ment[2 * JB];
+      if constexpr (R64) {
+        ment[0] = kh ? ev[2] : ev[0];
+        ment[1] = kh ? ev[3] : ev[1];
+      } else {
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) ment[pp] = ev[pp];
+        for (int pp = 0; pp < 4; ++pp) ment[pp] = ev[pp];
+      }
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb2 = 0; kb2 < JB; ++kb2) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           // key 32kb + 8i + 4hh + jj is row 8(i&1) + 4hh + jj of page 2kb + i/2
-          const int ent = ment[2 * kb + (i >> 1)];
+          const int ent = ment[2 * kb2 + (i >> 1)];
           int lim = (ent & 31) - 1;
           if (p.causal) lim = min(lim, thr - ent_slot(ent));
           const int rip0 = 8 * (i & 1) + 4 * hh;
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj)
-            if (rip0 + jj > lim) sacc[kb][4 * i + jj] = kNegInf;
+            if (rip0 + jj > lim) sacc[kb2][4 * i + jj] = kNegInf;
         }
       }
     }
-    float mt = fmaxf(max16(sacc[0]), max16(sacc[1]));
+    float mt = max16(sacc[0]);
+    if constexpr (JB == 2) mt = fmaxf(mt, max16(sacc[1]));
     mt = xor32_max(mt) * sl2;
     const bool grow = mt > mref + kLazySlack;
     if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -793,21 +829,18 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       mref = grow ? mt : mref;
     }
     const float nb = mref == kNegInf ? 0.f : -mref;
-    at(0);
     // all scalings, then all exponentials, each in place: 32 independent operations per step
     // instead of 32 dependent pairs through one temporary register
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb2 = 0; kb2 < JB; ++kb2)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[kb][e] = __builtin_fmaf(sacc[kb][e], sl2, nb);
-    pin(sacc[0]);
-    pin(sacc[1]);
+      for (int e = 0; e < 16; ++e) sacc[kb2][e] = __builtin_fmaf(sacc[kb2][e], sl2, nb);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (kb == 1) at(1);
+    for (int j2 = 0; j2 < JB; ++j2) pin(sacc[j2]);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[kb][e] = __builtin_amdgcn_exp2f(sacc[kb][e]);
-    }
+    for (int kb2 = 0; kb2 < JB; ++kb2)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[kb2][e] = __builtin_amdgcn_exp2f(sacc[kb2][e]);
     pin_vector_phase();
   };
 
@@ -842,7 +875,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
         transpose_write(transpose_read(vbuf));
         __builtin_amdgcn_sched_barrier(0);
         const SVec<4> next = entries(j + 3);
-        softmax(ej, j, [](int) {});
+        if (active) softmax(ej, j);
         wait_vmcnt<C::kInst>();  // K of the next stage landed
         bar();
         return next;
@@ -877,31 +910,51 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     wait_vmcnt<0>();  // loads past the list may still be landing in the stage buffers
   }
 
-  // ---- finish: combine lane halves, merge the two groups, write O and LSE ----
+  // ---- finish: combine lane halves, merge the states of each row group, write O and LSE ----
+  // States: one per group (128-row tiles), one per (group, key half) (64-row tiles).  Every
+  // state but (group 0, key half 0) goes to LDS as a record -- O^T in one of the four stage
+  // arrays, max and sum in the V^T array -- and that wave combines them.
   float l_tot = xor32_sum(l_run);
+  constexpr int kStates = R64 ? 4 : 2;                 // states per row group
+  const int sidx = R64 ? (2 * grp + kh) : grp;         // this wave's state
   __syncthreads();
-  float* mb = reinterpret_cast<float*>(wr == 0 ? sk0 : (wr == 1 ? sk1 : (wr == 2 ? sv0 : sv1)));
-  if (grp == 1) {
+  if (sidx != 0) {
+    const int rec = rg * (kStates - 1) + sidx - 1;     // 0 .. 3 (128-row) or 0 .. 5 (64-row)
+    uint8_t* arr = (rec >> 1) == 0 ? sk0 : ((rec >> 1) == 1 ? sk1 : ((rec >> 1) == 2 ? sv0 : sv1));
+    float* ob = reinterpret_cast<float*>(arr + (rec & 1) * C::kRecord);
+    float* mlb = reinterpret_cast<float*>(svt) + rec * 128;
 #pragma unroll
     for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mb[(db * 16 + e) * 64 + lane] = oacc[db][e];
-    mb[(C::kDB * 16) * 64 + lane] = mref;
-    mb[(C::kDB * 16 + 1) * 64 + lane] = l_tot;
+      for (int e = 0; e < 16; ++e) ob[(db * 16 + e) * 64 + lane] = oacc[db][e];
+    mlb[lane] = mref;
+    mlb[64 + lane] = l_tot;
   }
   __syncthreads();
-  if (grp == 1) return;
-  const float m1 = mb[(C::kDB * 16) * 64 + lane];
-  const float l1 = mb[(C::kDB * 16 + 1) * 64 + lane];
-  const float mm = fmaxf(mref, m1);
+  if (sidx != 0) return;
+  float mm = mref;
+#pragma unroll
+  for (int s = 1; s < kStates; ++s) mm = fmaxf(mm, reinterpret_cast<const float*>(svt)[(rg * (kStates - 1) + s - 1) * 128 + lane]);
   const float mu = (mm == kNegInf) ? 0.f : mm;
-  const float a0 = __builtin_amdgcn_exp2f(mref - mu);
-  const float a1 = __builtin_amdgcn_exp2f(m1 - mu);
+  {
+    const float a0 = __builtin_amdgcn_exp2f(mref - mu);
 #pragma unroll
-  for (int db = 0; db < C::kDB; ++db)
+    for (int db = 0; db < C::kDB; ++db) oacc[db] *= a0;
+    l_tot *= a0;
+  }
 #pragma unroll
-    for (int e = 0; e < 16; ++e) oacc[db][e] = oacc[db][e] * a0 + mb[(db * 16 + e) * 64 + lane] * a1;
-  l_tot = l_tot * a0 + l1 * a1;
+  for (int s = 1; s < kStates; ++s) {
+    const int rec = rg * (kStates - 1) + s - 1;
+    const uint8_t* arr = (rec >> 1) == 0 ? sk0 : ((rec >> 1) == 1 ? sk1 : ((rec >> 1) == 2 ? sv0 : sv1));
+    const float* ob = reinterpret_cast<const float*>(arr + (rec & 1) * C::kRecord);
+    const float* mlb = reinterpret_cast<const float*>(svt) + rec * 128;
+    const float a1 = __builtin_amdgcn_exp2f(mlb[lane] - mu);
+#pragma unroll
+    for (int db = 0; db < C::kDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[db][e] += ob[(db * 16 + e) * 64 + lane] * a1;
+    l_tot += mlb[64 + lane] * a1;
+  }
 
   if (!qvalid) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -922,6 +975,79 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 }
 
+// Block blk runs on XCD blk % 8 and is that XCD's (blk / 8)-th block.  The XCDs are split
+// into groups of kXcdShare; the groups take the (batch, head) slices in turn (group g: slices
+// g, g + 8 / kXcdShare, ...), and inside a group XCD x takes a contiguous chunk of each
+// slice's Q tiles.  Consecutive tiles of one XCD -- neighbouring Q blocks, whose K/V windows
+// overlap -- share its L2, and the slices in flight at a time, whose K/V the L2 misses
+// fetch, are few: 8 / kXcdShare of them.
+struct XcdList {
+  int c0, len;  // this XCD's tiles of each slice: [c0, c0 + len)
+  int g, G;     // its group, and the number of groups
+  int count;    // items of this XCD: len x slices of the group
+};
+__host__ __device__ inline XcdList xcd_list(int x, int n_qtiles, int BH) {
+  constexpr int S = kXcdShare;
+  XcdList l;
+  const int px = x % S;
+  l.G = 8 / S;
+  l.g = x / S;
+  l.c0 = px * n_qtiles / S;
+  l.len = (px + 1) * n_qtiles / S - l.c0;
+  const int nh = BH > l.g ? (BH - l.g + l.G - 1) / l.G : 0;
+  l.count = l.len * nh;
+  return l;
+}
+// work index (slice * n_qtiles + tile) of item i < l.count of an XCD's list
+__device__ __forceinline__ int xcd_work(const XcdList& l, int i, int n_qtiles) {
+  const int j = i / l.len;
+  return (l.g + j * l.G) * n_qtiles + l.c0 + (i - j * l.len);
+}
+// blocks per XCD a launch needs: the longest XCD list (of one or two shapes)
+static int xcd_rounds(int n1, int n2, int BH) {
+  int m = 0;
+  for (int x = 0; x < 8; ++x) m = std::max(m, xcd_list(x, n1, BH).count + xcd_list(x, n2, BH).count);
+  return m;
+}
+
+// Tiles of one shape (R64: the 64-row tiles), one workgroup per tile.
+template <int D, bool KPERM, bool R64>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) fwd_kernel_pp(FwdParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sk0[2 * PPCfg<D>::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t sk1[2 * PPCfg<D>::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t sv0[2 * PPCfg<D>::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t sv1[2 * PPCfg<D>::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t svt[2 * PPCfg<D>::kStage];
+  const PPSmem<D> sm{sk0, sk1, sv0, sv1, svt};
+  const int x = blockIdx.x & 7, i = blockIdx.x >> 3;
+  const XcdList l = xcd_list(x, p.n_qtiles, p.B * p.Hq);
+  if (i >= l.count) return;  // the grid covers the longest XCD list
+  pp_walk<D, KPERM, R64>(p, (const CONST_AS int32_t*)p.qtiles, p.n_qtiles, xcd_work(l, i, p.n_qtiles), sm);
+}
+
+// Both shapes in one launch: the 128-row tiles (qtiles, n_qtiles per slice) and the 64-row
+// tiles (qtiles2, n_qtiles2).  Each XCD takes its share of each kind, its 128-row tiles
+// first: the shorter 64-row tiles then fill the end of the launch, where XCDs would
+// otherwise wait for each other's last tiles.
+template <int D, bool KPERM>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) fwd_kernel_pp_fused(FwdParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sk0[2 * PPCfg<D>::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t sk1[2 * PPCfg<D>::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t sv0[2 * PPCfg<D>::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t sv1[2 * PPCfg<D>::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t svt[2 * PPCfg<D>::kStage];
+  const PPSmem<D> sm{sk0, sk1, sv0, sv1, svt};
+  const int x = blockIdx.x & 7, i = blockIdx.x >> 3, BH = p.B * p.Hq;
+  const XcdList a = xcd_list(x, p.n_qtiles, BH);
+  if (i < a.count) {
+    pp_walk<D, KPERM, false>(p, (const CONST_AS int32_t*)p.qtiles, p.n_qtiles, xcd_work(a, i, p.n_qtiles), sm);
+    return;
+  }
+  const XcdList c = xcd_list(x, p.n_qtiles2, BH);
+  if (i - a.count < c.count)
+    pp_walk<D, KPERM, true>(p, (const CONST_AS int32_t*)p.qtiles2, p.n_qtiles2, xcd_work(c, i - a.count, p.n_qtiles2), sm);
+}
+
 template <int D, int NRG, int NKG, int KB>
 static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
   if (p.n_work <= 0) return hipSuccess;
@@ -932,37 +1058,59 @@ static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-#ifndef BSATTN_KB128
-#define BSATTN_KB128 4
-#endif
-#ifndef BSATTN_KB64
-#define BSATTN_KB64 2
-#endif
-
-template <int D>
+template <int D, bool R64>
 static hipError_t launch_pp(const FwdParams& p, hipStream_t stream) {
   if (p.n_work <= 0) return hipSuccess;
+  const dim3 grid(8 * xcd_rounds(p.n_qtiles, 0, p.B * p.Hq));
   if (p.kperm)
-    hipLaunchKernelGGL((fwd_kernel_pp<D, true>), dim3(p.n_work), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel_pp<D, true, R64>), grid, dim3(512), 0, stream, p);
   else
-    hipLaunchKernelGGL((fwd_kernel_pp<D, false>), dim3(p.n_work), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel_pp<D, false, R64>), grid, dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
-// The ping-pong kernel runs 128x128 tiles unless keys are permuted under a causal mask (its
-// mask reads no key tokens) or the permuted offsets would not fit 24-bit products.
+template <int D>
+static hipError_t launch_pp_fused(const FwdParams& p, hipStream_t stream) {
+  if (p.n_work + p.n_work2 <= 0) return hipSuccess;
+  const dim3 grid(8 * xcd_rounds(p.n_qtiles, p.n_qtiles2, p.B * p.Hq));
+  if (p.kperm)
+    hipLaunchKernelGGL((fwd_kernel_pp_fused<D, true>), grid, dim3(512), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fwd_kernel_pp_fused<D, false>), grid, dim3(512), 0, stream, p);
+  return hipGetLastError();
+}
+
+// The ping-pong walk runs both shapes unless keys are permuted under a causal mask (its mask
+// reads no key tokens) or the permuted offsets would not fit 24-bit products; those problems
+// go to the 4-wave kernel above (128-row tiles: 4 row groups x 128-key tiles; 64-row tiles:
+// 2 row groups x 2 key groups of 64 keys).
 static bool pp_supported(const FwdParams& p) {
   if (!p.kperm) return true;
   return !p.causal && p.Nk < (1 << 24) && p.k_sn_bytes < (1u << 24) && p.v_sn_bytes < (1u << 24);
 }
 
+template <int D>
+static hipError_t launch_shape_d(const FwdParams& p, int shape, hipStream_t stream) {
+  if (shape == 0) return pp_supported(p) ? launch_pp<D, false>(p, stream) : launch_one<D, 4, 1, 4>(p, stream);
+  return pp_supported(p) ? launch_pp<D, true>(p, stream) : launch_one<D, 2, 2, 2>(p, stream);
+}
+
 hipError_t launch_fwd_shape(const FwdParams& p, int shape, int d, hipStream_t stream) {
-  if (d == 128) {
-    if (shape == 0) return pp_supported(p) ? launch_pp<128>(p, stream) : launch_one<128, 4, 1, BSATTN_KB128>(p, stream);
-    return launch_one<128, 2, 2, BSATTN_KB64>(p, stream);
-  }
-  if (shape == 0) return pp_supported(p) ? launch_pp<64>(p, stream) : launch_one<64, 4, 1, BSATTN_KB128>(p, stream);
-  return launch_one<64, 2, 2, BSATTN_KB64>(p, stream);
+  return d == 128 ? launch_shape_d<128>(p, shape, stream) : launch_shape_d<64>(p, shape, stream);
+}
+
+// Both shapes: one fused launch when the ping-pong walk supports the problem, else one
+// launch per shape.  p describes the 128-row tiles (qtiles, n_qtiles, n_work) and p.qtiles2,
+// n_qtiles2, n_work2 the 64-row ones.
+hipError_t launch_fwd(const FwdParams& p, int d, hipStream_t stream) {
+  if (pp_supported(p)) return d == 128 ? launch_pp_fused<128>(p, stream) : launch_pp_fused<64>(p, stream);
+  FwdParams p2 = p;
+  p2.qtiles = p.qtiles2;
+  p2.n_qtiles = p.n_qtiles2;
+  p2.n_work = p.n_work2;
+  hipError_t e = launch_fwd_shape(p, 0, d, stream);
+  if (e != hipSuccess) return e;
+  return launch_fwd_shape(p2, 1, d, stream);
 }
 
 }  // namespace bsattn

@@ -5,6 +5,9 @@
 
 namespace bsattn {
 
+// XCDs (of the chip's 8) that work on one (batch, head) slice of the forward at a time.
+constexpr int kXcdShare = 1;
+
 // One Q tile as the kernel reads it.
 struct QTileDev {
   int32_t row0;    // first slot in the Q layout
@@ -23,7 +26,8 @@ struct FwdParams {
   int64_t k_sb, k_sn, k_sh;
   int64_t v_sb, v_sn, v_sh;
   int64_t o_sb, o_sn, o_sh;
-  const QTileDev* qtiles;     // Q tiles of one shape
+  const QTileDev* qtiles;     // Q tiles of one shape (the 128-row tiles in a launch of both)
+  const QTileDev* qtiles2;    // a launch of both shapes: the 64-row tiles
   const int32_t* pl_ptr;      // [n_units * nqb + 1]
   const int32_t* pl_ent;      // packed (first slot << 5) | valid rows
   const int32_t* qperm;       // slot -> token, or null
@@ -33,6 +37,7 @@ struct FwdParams {
   uint32_t k_sn_bytes, v_sn_bytes;
   int32_t n_qtiles;           // tiles of this shape
   int32_t n_work;             // n_qtiles * B * Hq
+  int32_t n_qtiles2, n_work2; // a launch of both shapes: the same for the 64-row tiles
   int32_t B, Hq, Hkv, Nq, Nk, grp;
   int32_t nqb, sel_nh, ub_mul, uh_div;
   int32_t causal;

@@ -107,6 +107,17 @@ RANDOM_CASES = [
          density=1.0),
     dict(seed=108, B=1, Hq=2, Hkv=2, Nq=64, Nk=16, d=64, max_qblock=64, max_kblock=16, sel_mode="head",
          density=1.0),
+    # head dim 128 with permuted keys under a causal mask: the 4-wave kernel for both shapes
+    dict(seed=109, B=1, Hq=2, Hkv=1, Nq=520, Nk=610, d=128, max_qblock=150, max_kblock=45, sel_mode="kv",
+         causal=True, use_perm=True, allow_empty=True, density=0.35),
+    # 64-row tiles of every size (1..64 rows: some with one row group, some with two) and
+    # 128-row tiles of 65..128 rows, causal with identity layouts
+    dict(seed=110, B=1, Hq=2, Hkv=2, Nq=900, Nk=700, d=128, max_qblock=128, max_kblock=60, sel_mode="head",
+         causal=True, q_pos0=-50, density=0.4),
+    # rows with 0-18 keys in tiles of both shapes: the log-sum-exp of a row of one or two keys
+    # shows any rounding of the probabilities in the row sum
+    dict(seed=115, B=1, Hq=2, Hkv=2, Nq=640, Nk=300, d=128, max_qblock=128, max_kblock=4, sel_mode="head",
+         density=0.01, allow_empty=True),
 ]
 
 
@@ -115,7 +126,7 @@ def test_random_full(kw):
     check_full(make_random(**kw), f"random-{kw['seed']}")
 
 
-@pytest.mark.parametrize("case", ["tiny3d", "seed103", "seed105"])
+@pytest.mark.parametrize("case", ["tiny3d", "seed103", "seed105", "seed109"])
 def test_fixed_tiles_plan_same_results(case):
     # the fixed-tile baseline plan (no packing, no 64-row routing) runs the same kernels
     # with padded page slots and must give the same results
@@ -128,6 +139,28 @@ def test_fixed_tiles_plan_same_results(case):
     O, L, _ = run_gpu(w, plan=plan)
     Or, Lr = masked_attention_w(w)
     check_rows(np.transpose(O, (0, 2, 1, 3)), L, np.transpose(Or, (0, 2, 1, 3)), Lr, f"fixed-{case}")
+
+
+def _run_split(w, plan):
+    """Both tile shapes launched one by one (bsattn_fwd_shape), NaN-poisoned outputs."""
+    q, k, v = _dev(w.q), _dev(w.k), _dev(w.v)
+    o = torch.full((w.B, w.Nq, w.Hq, w.d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((w.B, w.Hq, w.Nq), float("nan"), dtype=torch.float32, device="cuda")
+    for sh in (bs.SHAPE_64x256, bs.SHAPE_128x128):
+        plan.fwd(q, k, v, o, lse, scale=w.scale, shape=sh)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("case", ["seed101", "seed102", "seed104", "seed109", "seed110"])
+def test_one_launch_equals_shape_launches(case):
+    # bsattn_fwd runs both shapes in one launch (where the ping-pong walk takes the problem);
+    # each tile computes the same bits as in its own shape's launch
+    w = make_random(**[c for c in RANDOM_CASES if f"seed{c['seed']}" == case][0])
+    _say(f"[gpu] one launch vs shape launches {case}: Nq={w.Nq} d={w.d} causal={w.causal} perm={w.k_perm is not None}")
+    O1, L1, plan = run_gpu(w)
+    O2, L2 = _run_split(w, plan)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
 
 
 def test_block_order_hint_same_bits():
