@@ -214,8 +214,9 @@ def test_decode_geometry_and_unsupported_plans():
     assert e.value.status == 4
     per_head = make_random(9, B=1, Hq=4, Hkv=2, Nq=20, Nk=100, d=64, max_qblock=4, sel_mode="head",
                            with_tensors=False)
+    ph = bs.Plan.from_workload(per_head)  # held: a temporary Plan is destroyed before the call
     with pytest.raises(bs.BsattnError) as e:
-        bs.bsattn_decode_workspace_bytes(bs.Plan.from_workload(per_head).handle)
+        bs.bsattn_decode_workspace_bytes(ph.handle)
     assert e.value.status == 4
 
 
