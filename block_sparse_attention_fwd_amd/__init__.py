@@ -21,7 +21,7 @@ __all__ = [
     "bsattn_plan_create", "bsattn_plan_create_ex", "bsattn_plan_set_block_order", "PLAN_FIXED_TILES", "bsattn_plan_device_bytes", "bsattn_plan_upload", "bsattn_plan_stats",
     "bsattn_plan_export", "bsattn_plan_export_bwd", "PlanBwdView", "bsattn_fwd", "bsattn_fwd_shape",
     "bsattn_bwd_workspace_bytes", "bsattn_bwd", "bsattn_chunk_select", "ChunkProblem", "chunk_select",
-    "bsattn_decode_workspace_bytes", "bsattn_fwd_decode", "bsattn_plan_update_selection",
+    "bsattn_decode_workspace_bytes", "bsattn_fwd_decode", "bsattn_fwd_decode_noalloc", "bsattn_plan_update_selection",
     "bsattn_plan_destroy", "bsattn_status_string", "bsattn_last_hip_error", "SHAPE_128x128", "SHAPE_64x256", "PAGE_SIZE",
 ]
 
@@ -95,7 +95,8 @@ _lib: Optional[ctypes.CDLL] = None
 EXPORTED = ["bsattn_plan_create", "bsattn_plan_create_ex", "bsattn_plan_set_block_order", "bsattn_plan_device_bytes", "bsattn_plan_upload", "bsattn_plan_stats",
             "bsattn_plan_export", "bsattn_plan_export_bwd", "bsattn_fwd", "bsattn_fwd_shape",
             "bsattn_bwd_workspace_bytes", "bsattn_bwd", "bsattn_chunk_select", "bsattn_decode_workspace_bytes",
-            "bsattn_fwd_decode", "bsattn_plan_update_selection", "bsattn_plan_destroy", "bsattn_status_string",
+            "bsattn_fwd_decode", "bsattn_fwd_decode_noalloc", "bsattn_plan_update_selection", "bsattn_plan_destroy",
+            "bsattn_status_string",
             "bsattn_last_hip_error"]
 
 
@@ -125,6 +126,7 @@ def library() -> ctypes.CDLL:
     lib.bsattn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, ctypes.c_size_t, vp]
     lib.bsattn_decode_workspace_bytes.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t)]
     lib.bsattn_fwd_decode.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, ctypes.c_size_t, vp]
+    lib.bsattn_fwd_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp]
     lib.bsattn_plan_update_selection.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp]
     lib.bsattn_chunk_select.argtypes = [ctypes.POINTER(ChunkProblem), vp, vp, vp, vp, vp]
     lib.bsattn_plan_destroy.argtypes = [vp]
@@ -268,6 +270,15 @@ def bsattn_fwd_decode(plan, q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_
     vp = ctypes.c_void_p
     _check(library().bsattn_fwd_decode(plan, vp(q_ptr), vp(k_ptr), vp(v_ptr), vp(o_ptr), vp(lse_ptr),
                                        ctypes.c_float(scale), vp(ws_ptr), ws_bytes, vp(stream)), "bsattn_fwd_decode")
+
+
+def bsattn_fwd_decode_noalloc(plan, q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, scale: float,
+                              stream: int = 0) -> None:
+    """bsattn_fwd_decode with the library's own device buffer for the partial states (no
+    workspace argument, no allocation; calls overlapping on one GPU race)."""
+    vp = ctypes.c_void_p
+    _check(library().bsattn_fwd_decode_noalloc(plan, vp(q_ptr), vp(k_ptr), vp(v_ptr), vp(o_ptr), vp(lse_ptr),
+                                               ctypes.c_float(scale), vp(stream)), "bsattn_fwd_decode_noalloc")
 
 
 def bsattn_plan_update_selection(plan, n_b: int, n_h: int, row_ptr_ptr: int, kblk_ptr: int, status_ptr: int = 0,

@@ -17,6 +17,7 @@ hipError_t launch_bwd(const BwdParams& p, int d, hipStream_t stream);
 hipError_t launch_chunk_select(const ChunkParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t stream);
 hipError_t launch_plan_update(const PlanUpdateParams& p, hipStream_t stream);
+hipError_t decode_scratch(void** ptr, size_t* bytes);
 }
 
 namespace {
@@ -417,6 +418,22 @@ int bsattn_fwd_decode(const bsattn_plan* plan, const void* q, const void* k, con
   hipError_t e = bsattn::launch_decode(dp, pr.d, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e);
   return BSATTN_OK;
+}
+
+int bsattn_fwd_decode_noalloc(const bsattn_plan* plan, const void* q, const void* k, const void* v, void* o,
+                              float* lse, float scale, void* stream) {
+  if (plan == nullptr) return BSATTN_E_ARG;
+  int32_t ns = 0, per = 0;
+  size_t need = 0;
+  const int st = decode_geometry(plan, &ns, &per, &need);
+  if (st != BSATTN_OK) return st;
+  if (need > bsattn::kDecodeScratchBytes) return BSATTN_E_UNSUPPORTED;
+  if (plan->dev == nullptr) return BSATTN_E_STATE;
+  void* ws = nullptr;
+  size_t bytes = 0;
+  const hipError_t e = bsattn::decode_scratch(&ws, &bytes);
+  if (e != hipSuccess) return hip_fail(e);
+  return bsattn_fwd_decode(plan, q, k, v, o, lse, scale, ws, bytes, stream);
 }
 
 int bsattn_chunk_select(const bsattn_chunk_problem* pr, const void* q, const void* k, float* summaries,

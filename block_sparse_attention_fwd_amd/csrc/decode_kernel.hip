@@ -19,6 +19,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "device_common.hpp"
 #include "kernel_params.hpp"
@@ -315,6 +316,34 @@ hipError_t launch_decode_d(const DecodeParams& p, hipStream_t stream) {
 
 hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t stream) {
   return d == 128 ? launch_decode_d<128>(p, stream) : launch_decode_d<64>(p, stream);
+}
+
+// Partial softmax states for bsattn_fwd_decode_noalloc, whose callers cannot allocate device
+// memory: a buffer in the library's own device data.  Every GPU the library runs on holds its
+// own copy until the process ends; in host code the name is only a host-side stand-in, so the
+// kernels get the device address looked up below.
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
+// Device address of the current GPU's scratch array: looked up on the first call on each
+// device (that device current) and kept per device.
+hipError_t decode_scratch(void** ptr, size_t* bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  *bytes = kDecodeScratchBytes;
+  return hipSuccess;
 }
 
 }  // namespace bsattn

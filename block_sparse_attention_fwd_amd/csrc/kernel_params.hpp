@@ -1,6 +1,7 @@
 // Arguments of the forward and backward kernels (passed by value) and the device tile record.
 #pragma once
 
+#include <cstddef>
 #include <cstdint>
 
 namespace bsattn {
@@ -106,6 +107,9 @@ struct DecodeParams {
   int32_t causal;
   float scale, scale_log2;
 };
+
+// Bytes of the library-held device buffer behind bsattn_fwd_decode_noalloc (per GPU).
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
 
 // Page lists rebuilt on the device from a device-resident selection.
 struct PlanUpdateParams {

@@ -288,6 +288,18 @@ int bsattn_decode_workspace_bytes(const bsattn_plan* plan, size_t* bytes);
 int bsattn_fwd_decode(const bsattn_plan* plan, const void* q, const void* k, const void* v, void* o,
                       float* lse, float scale, void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, serving
+ * loops, harnesses that forbid hipMalloc): bsattn_fwd_decode with the partial states in a
+ * buffer the library holds in its own device data, 16 MiB per GPU (kept until the process
+ * ends), instead of a caller workspace.  Allocates nothing.  Every call on one GPU uses that
+ * GPU's one buffer: calls that overlap on a GPU (on different streams, or from different
+ * threads) race and must be ordered by the caller; each call writes every partial state it
+ * reads, so nothing carries over from an earlier call.  Same arguments (without the
+ * workspace), results and errors as bsattn_fwd_decode; BSATTN_E_UNSUPPORTED also when
+ * bsattn_decode_workspace_bytes exceeds 16 MiB (checked before the upload state). */
+int bsattn_fwd_decode_noalloc(const bsattn_plan* plan, const void* q, const void* k, const void* v, void* o,
+                              float* lse, float scale, void* stream);
+
 /* Chunk selection (CISA abstract, fugumt page 4, sentences 3-5: fixed-size KV chunks
  * chosen with compact summaries of the keys, one indexing query per KV group, the selection
  * shared by the group's queries).  Q [B, Nq, Hq, d] and K [B, Nk, Hkv, d] are bf16 with the

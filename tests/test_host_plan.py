@@ -220,6 +220,30 @@ def test_decode_geometry_and_unsupported_plans():
     assert e.value.status == 4
 
 
+def test_decode_noalloc_limits():
+    # the allocation-free decode holds its partial states in a 16 MiB library buffer: plans
+    # needing more are rejected before anything touches a GPU, and so are plans the decode
+    # path does not take; a fitting plan that was never uploaded is a state error
+    many = make_random(21, B=1, Hq=8, Hkv=8, Nq=420, Nk=64, d=128, max_qblock=4, max_kblock=16, sel_mode="kv",
+                       density=0.5, with_tensors=False)
+    pm = bs.Plan.from_workload(many)
+    assert bs.bsattn_decode_workspace_bytes(pm.handle) > 16 << 20
+    with pytest.raises(bs.BsattnError) as e:
+        bs.bsattn_fwd_decode_noalloc(pm.handle, 16, 16, 16, 16, 16, 0.125, 0)
+    assert e.value.status == 4
+    big = make_random(8, B=1, Hq=8, Hkv=1, Nq=100, Nk=100, d=64, max_qblock=20, sel_mode="kv", with_tensors=False)
+    pb = bs.Plan.from_workload(big)
+    with pytest.raises(bs.BsattnError) as e:
+        bs.bsattn_fwd_decode_noalloc(pb.handle, 16, 16, 16, 16, 16, 0.125, 0)
+    assert e.value.status == 4
+    w = make_chunk_gqa("decode", 7, B=2, Hq=16, Hkv=2, d=128, Nk=64 * 150, Nq=1, chunk=64, topk=40)
+    p = bs.Plan.from_workload(w)
+    assert bs.bsattn_decode_workspace_bytes(p.handle) <= 16 << 20
+    with pytest.raises(bs.BsattnError) as e:
+        bs.bsattn_fwd_decode_noalloc(p.handle, 16, 16, 16, 16, 16, 0.125, 0)
+    assert e.value.status == 7
+
+
 def test_update_selection_needs_upload():
     w = make_random(12, B=1, Hq=2, Hkv=2, Nq=40, Nk=40, d=64, sel_mode="kv", with_tensors=False)
     p = bs.Plan.from_workload(w)
