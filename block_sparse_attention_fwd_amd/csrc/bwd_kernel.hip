@@ -1,8 +1,8 @@
 // Exact block-sparse attention backward for gfx950 (MI355X).
 //
 // The gradients are those of masked softmax attention (KPage abstract, zhuanzhiai page 1,
-// sentence 4: exact masking and K/V-owned page packing keep the original sparse graph in
-// backward execution).  With P^ = exp(S - LSE) on the graph's pairs and 0 elsewhere:
+// sentence 4): gradients are computed only on the pairs of the selected sparse graph, and
+// every dK/dV row is owned by one K/V tile.  With P^ = exp(S - LSE) on the graph's pairs and 0 elsewhere:
 //   D_i   = sum_e dO_ie O_ie                                   (bwd_dot_kernel)
 //   dV_j  = sum_i P^_ij dO_i,  dK_j = scale sum_i dS_ij Q_i    (bwd_dkdv_kernel)
 //   dS_ij = P^_ij (dO_i . V_j - D_i),  dQ_i = scale sum_j dS_ij K_j   (bwd_dq_kernel)

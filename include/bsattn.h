@@ -250,8 +250,8 @@ int bsattn_fwd_shape(const bsattn_plan* plan, int32_t shape, const void* q, cons
 int bsattn_bwd_workspace_bytes(const bsattn_plan* plan, size_t* bytes);
 
 /* The backward pass: gradients of the same masked softmax attention (KPage abstract,
- * sentence 4: exact masking and K/V-owned pages keep the sparse graph in backward
- * execution).  With P^ = exp(scale <Q_i, K_j> - LSE_i) on the graph's pairs and 0 elsewhere,
+ * sentence 4: the backward works on the selected pairs only, with pages owned by one K/V
+ * block).  With P^ = exp(scale <Q_i, K_j> - LSE_i) on the graph's pairs and 0 elsewhere,
  * dO the gradient of O and D_i = sum_e dO_ie O_ie:
  *     dV[b, j, g, :] = sum over the query heads h of group g, sum_i P^_ij dO[b, i, h, :]
  *     dS_ij          = P^_ij (<dO[b, i, h, :], V[b, j, g, :]> - D_i)

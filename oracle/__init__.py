@@ -21,8 +21,9 @@ Contents
 Sources (cited by page title and passage):
   * KPage abstract (zhuanzhiai page 1): sentence 2 (16-row K/V pages of valid tokens,
     packed across block boundaries into large tiles while loading), sentence 3 (Q
-    blocks routed between 64x256 and 128x128 tiles), sentence 4 (exact masking keeps
-    the original sparse graph), sentence 7 (physical vs useful query-key pairs).
+    blocks routed between 64x256 and 128x128 tiles), sentence 4 (pages belong to one
+    K/V block and masking is exact: only the selected graph's pairs count), sentence 7
+    (physical vs useful query-key pairs).
   * CISA abstract (fugumt page 4): sentences 3-5 (KV chunks selected per KV group and
     shared by the group's queries) -- the selection is an input here.
   * FlashAttention entries of the related-paper lists (scifaro pages 2 and 3): exact

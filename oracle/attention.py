@@ -2,8 +2,8 @@
 
 Test infrastructure only (see the package docstring).
 
-What is computed (KPage abstract, sentences 2 and 4: packing and exact masking keep
-the original sparse graph, so the result is plain masked softmax attention):
+What is computed (KPage abstract, sentences 2 and 4: packing changes only how pairs are
+grouped into tiles and masking is exact, so the result is plain masked softmax attention):
 
   For batch b, query head h with KV head g = h // (Hq / Hkv), query token i and key
   token j, the pair (i, j) is in the graph iff the K block holding j is in the
@@ -245,8 +245,8 @@ def brute_force_attention(q, k, v, q_offsets, q_perm, k_offsets, k_perm, sel_nb,
 # ----------------------------------------------------------------------------
 # backward: gradients of the same masked softmax attention
 # ----------------------------------------------------------------------------
-# KPage abstract, sentence 4: masking and K/V-owned pages keep the original sparse graph in
-# the backward pass as well, so the gradients are those of the function above.  With
+# KPage abstract, sentence 4: the backward works on the same selected pairs (pages owned by
+# one K/V block, exact masking), so the gradients are those of the function above.  With
 # P^_ij = exp(S_ij - LSE_i) (zero outside the graph and on rows without keys) and an
 # upstream gradient dO of O, the chain rule through O = P^ V and the row softmax gives
 #     D_i   = sum_e dO_ie O_ie

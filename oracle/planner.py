@@ -3,8 +3,8 @@
 KPage abstract, sentence 2: keys and values are cut into 16-row pages of valid tokens,
 and pages are packed across logical-block boundaries into large tiles while loading.
 Sentence 3: Q blocks are routed between 64x256 and 128x128 tiles to cut query-side
-padding.  Sentence 4: each page is owned by one K/V block ("K/V-owned"), so exact
-masking keeps the sparse graph.  Sentence 7: physical query-key pair capacity (what the
+padding.  Sentence 4: each page belongs to one K/V block and masking is exact, so only
+the selected graph's pairs count.  Sentence 7: physical query-key pair capacity (what the
 tiles hold, padding included) versus useful pairs (the graph's edges).
 
 Readings of what the abstract leaves open (one per rule):
@@ -208,8 +208,8 @@ def build_plan_w(w, fixed_tiles=False) -> Plan:
 # ----------------------------------------------------------------------------
 # backward tables
 # ----------------------------------------------------------------------------
-# KPage abstract, sentence 4: K/V-owned page packing keeps the sparse graph in backward
-# execution.  Readings: the key side owns its rows -- each K block is cut into 64-slot tiles
+# KPage abstract, sentence 4: the backward also walks pages that each belong to one
+# K/V block, on the selected pairs only.  Readings: the key side owns its rows -- each K block is cut into 64-slot tiles
 # (ceil(n/64) per block, the last one short) -- and the query side is streamed in 16-row Q
 # pages (a Q block of n slots has ceil(n/16) pages, as the K side in R2).  For each
 # (unit, K block) the Q pages to visit are those of every Q block whose selection row holds
