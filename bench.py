@@ -484,7 +484,8 @@ def main():
                 # from the same counter runs (MFMA busy share of active SIMD cycles, LDS bank-conflict cycles)
                 "mfma_busy_pct": float(kv[f"{tag}.mfma_busy_pct"]) if f"{tag}.mfma_busy_pct" in kv else None,
                 "lds_bank_conflict_cycles": int(kv[f"{tag}.lds_bank_conflict_cycles"])
-                if f"{tag}.lds_bank_conflict_cycles" in kv else None}
+                if f"{tag}.lds_bank_conflict_cycles" in kv else None,
+                "l2_hit_pct": float(kv[f"{tag}.l2_hit_pct"]) if f"{tag}.l2_hit_pct" in kv else None}
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -515,14 +516,14 @@ def main():
                    "plan": "fixed 128x128 tiles per selected block pair (no packing)" if args.fixed_tiles
                    else "packed pages, routed Q tiles",
                    "dispatch_order": "Q blocks in order" if (args.natural_order or w.q_block_order is None)
-                   else "workload hint (cubes by h, t, w)",
+                   else "workload hint (cubes in slabs of two w columns, then t, h, w)",
                    "plan_ms": round(t_plan * 1e3, 2)},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     if args.fixed_tiles or args.natural_order:
         # the counter runs cover the default plan and order only
-        for key in ("traffic", "hbm_GBps", "hbm_frac", "mfma_busy_pct", "lds_bank_conflict_cycles"):
+        for key in ("traffic", "hbm_GBps", "hbm_frac", "mfma_busy_pct", "lds_bank_conflict_cycles", "l2_hit_pct"):
             roofline[key] = None
     print(json.dumps(out), flush=True)
 

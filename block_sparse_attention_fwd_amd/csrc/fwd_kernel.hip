@@ -421,10 +421,11 @@ __global__ void __launch_bounds__(256)
 //                  16 MFMAs per matrix phase.  Four consecutive stages are one 256-key K
 //                  tile of the plan; two groups x two slots keep all four in LDS at once.
 // Each (group, key half) keeps its own softmax state over its keys; the states of a row
-// group are merged through LDS at the end.  In a 64-row tile of at most 32 valid rows, the
-// waves of the second row group skip their products and exponentials but keep their share
-// of the loads, the V transposition and every barrier.  Both shapes use the same LDS stage
-// layout, so one launch can run tiles of both kinds.
+// group are merged through LDS at the end.  The waves of a row group that holds only
+// padding (rows past the tile's valid count) walk a copy of the loop without products and
+// exponentials: they keep their share of the loads, the V transposition and every barrier.
+// The branch is taken once per tile, so the busy waves run branch-free phases.  Both shapes
+// use the same LDS stage layout, so one launch can run tiles of both kinds.
 //
 // The softmax reference max is lazy: it moves only when a stage's max exceeds it by more
 // than 2^8 in exp2 units, so O is rescaled a few times per tile instead of at most stages.
@@ -497,10 +498,8 @@ __device__ __forceinline__ void pp_walk(const FwdParams& p, const CONST_AS int32
   const int e1 = pl_ptr[row + 1];
   const int ns = (e1 - e0 + 3) >> 2;        // 64-key stages
   const int my_n = (ns + 1 - grp) >> 1;     // this group's stages: global 2j + grp, j < my_n
-  // A row group of a 64-row tile past the tile's valid rows holds only padding: no products
-  // for it (uniform).  The 128-row tiles keep every row group busy: skipping there measured
-  // slower on the video-DiT layout (its code then branches in every phase).
-  const bool active = R64 ? rg * 32 < qt_rows : true;
+  // a row group past the tile's valid rows holds only padding: no products for it (uniform)
+  const bool active = rg * 32 < qt_rows;
 
   // ---- Q^T operand: lane holds query (lane % 32) of its row group, 8 d per k-step ----
   const int qrow = rg * 32 + (lane & 31);
@@ -670,17 +669,17 @@ __device__ __forceinline__ void pp_walk(const FwdParams& p, const CONST_AS int32
   // Matrix phase: O^T += V^T P^T over the staged V^T operands (PV), then S^T = K Q^T over the
   // K stage at kb (QK).  The products run as one list (PV: 16-key chunk c, d block db; QK:
   // k-step s, key block j) whose operands are read kLead products ahead of their use, so
-  // the matrix core does not stall on LDS latency between products.  A wave without valid
-  // rows issues only the loads.
+  // the matrix core does not stall on LDS latency between products.  Without ACT (a wave
+  // with no valid rows) the phase issues only the loads.
   constexpr int kNPV = 2 * JB * C::kDB, kNQK = JB * C::kDS, kLead = 4;
   auto mphase = [&](const uint8_t* kb, auto pv_tag, auto qk_tag, const PageLoad* ldk, uint8_t* kdst, const PageLoad* ldv,
-                    uint8_t* vdst) __attribute__((always_inline)) {
-    constexpr bool PV = decltype(pv_tag)::value, QK = decltype(qk_tag)::value;
+                    uint8_t* vdst, auto act_tag) __attribute__((always_inline)) {
+    constexpr bool PV = decltype(pv_tag)::value, QK = decltype(qk_tag)::value, ACT = decltype(act_tag)::value;
     constexpr int n0 = PV ? 0 : kNPV;
     constexpr int n1 = QK ? kNPV + kNQK : kNPV;
     constexpr int kSpread = (n1 - n0) / (2 * C::kInst);  // one load before every kSpread-th product
     static_assert(kSpread >= 1, "a product per load");
-    if (!active) {
+    if constexpr (!ACT) {
       if (ldk) {
 #pragma unroll
         for (int n = 0; n < C::kInst; ++n) fire(*ldk, krsrc, kdst, n);
@@ -858,14 +857,16 @@ __device__ __forceinline__ void pp_walk(const FwdParams& p, const CONST_AS int32
     wait_vmcnt<C::kInst>();  // K of stage 0 landed
     bar();
     if (grp == 1) bar();  // group 1 runs one phase behind
-    if (my_n > 0) {
+    // the walk; a wave whose row group holds only padding runs it without products
+    auto walk = [&](auto act_tag) __attribute__((always_inline)) {
+      constexpr bool ACT = decltype(act_tag)::value;
       // matrix phase: P.V of the previous stage (if PV), S of the stage in kbuf (if QK), loads
       // of stage jn (entry word ent) into kdst / vdst
       auto mph = [&](auto pv_tag, auto qk_tag, const uint8_t* kbuf, int ent, uint8_t* kdst, uint8_t* vdst)
                      __attribute__((always_inline)) {
         const PageLoad lk = prep(ent, p.k_sn_bytes, ld_vk);
         const PageLoad lv = prep(ent, p.v_sn_bytes, ld_vv);
-        mphase(kbuf, pv_tag, qk_tag, &lk, kdst, &lv, vdst);
+        mphase(kbuf, pv_tag, qk_tag, &lk, kdst, &lv, vdst, act_tag);
         wait_vmcnt<2 * C::kInst>();  // V of the phase's own stage landed
         bar();
       };
@@ -875,7 +876,7 @@ __device__ __forceinline__ void pp_walk(const FwdParams& p, const CONST_AS int32
         transpose_write(transpose_read(vbuf));
         __builtin_amdgcn_sched_barrier(0);
         const SVec<4> next = entries(j + 3);
-        if (active) softmax(ej, j);
+        if constexpr (ACT) softmax(ej, j);
         wait_vmcnt<C::kInst>();  // K of the next stage landed
         bar();
         return next;
@@ -899,8 +900,14 @@ __device__ __forceinline__ void pp_walk(const FwdParams& p, const CONST_AS int32
         mph(BoolTag<true>{}, BoolTag<true>{}, sk1, mine(x1, j + 1), sk0, sv0);
         vph(j, x0, sv1);
       }
-      mphase(sk0, BoolTag<true>{}, BoolTag<false>{}, nullptr, nullptr, nullptr, nullptr);  // P.V of the last stage
+      mphase(sk0, BoolTag<true>{}, BoolTag<false>{}, nullptr, nullptr, nullptr, nullptr, act_tag);  // P.V of the last stage
       bar();
+    };
+    if (my_n > 0) {
+      if (active)
+        walk(BoolTag<true>{});
+      else
+        walk(BoolTag<false>{});
     }
     // both groups pass the same number of barriers
     const int n0 = (ns + 1) >> 1, n1 = ns >> 1;
