@@ -405,13 +405,12 @@ __global__ void __launch_bounds__(256)
 // tile's 64-key stages (4 pages): group g takes stages g, g + 2, g + 4, ...  The walk
 // alternates two kinds of phase between workgroup barriers: a matrix phase (P.V of the
 // group's previous stage, then S^T = K Q^T of its current one) and a vector phase (mask,
-// online softmax and exponentials of the current stage, plus transposing the stage's V into
-// ready-made MFMA operands in LDS).  Group 1 runs one phase behind group 0, so in every phase
-// each SIMD holds one wave issuing MFMAs and one issuing vector instructions, and the two
-// execute side by side.  Staging V^T moves the transposing LDS reads out of the matrix phase,
-// whose every operand is then a single 16-byte read (a wave can only keep a few LDS reads in
-// flight, so their count bounds the matrix phase).  K and V stages are double-buffered per
-// group and loaded two to three phases before they are read.
+// online softmax and exponentials of the current stage).  Group 1 runs one phase behind
+// group 0, so in every phase each SIMD holds one wave issuing MFMAs and one issuing vector
+// instructions, and the two execute side by side.  The P.V products read their V^T operands
+// straight from the V stage with transposing LDS reads (two per operand).  K and V stages
+// are double-buffered per group: the matrix phase issues the next stage's K pages, the
+// vector phase (which no longer touches LDS) the next stage's V pages.
 //
 // The two Q-tile shapes of the plan (KPage abstract, zhuanzhiai page 1, sentence 3) differ
 // only in how a group's four waves share a stage:
@@ -423,7 +422,7 @@ __global__ void __launch_bounds__(256)
 // Each (group, key half) keeps its own softmax state over its keys; the states of a row
 // group are merged through LDS at the end.  The waves of a row group that holds only
 // padding (rows past the tile's valid count) walk a copy of the loop without products and
-// exponentials: they keep their share of the loads, the V transposition and every barrier.
+// exponentials: they keep their share of the loads and every barrier.
 // The branch is taken once per tile, so the busy waves run branch-free phases.  Both shapes
 // use the same LDS stage layout, so one launch can run tiles of both kinds.
 //
@@ -440,22 +439,24 @@ struct PPCfg {
   static constexpr int kStage = 64 * kRowBytes;       // one 64-key stage of K or V
   static constexpr int kDS = D / 16;                  // k-steps of QK^T
   static constexpr int kDB = D / 32;                  // 32-wide d blocks of O^T
-  // a wave's end state for the merge: O^T accumulators (kDB x 16 floats per lane)
+  // a wave's end state for the merge: O^T accumulators (kDB x 16 floats per lane), and
+  // max and sum of up to six records (64 lanes each)
   static constexpr int kRecord = kDB * 16 * 64 * 4;
+  static constexpr int kMlBytes = 6 * 2 * 64 * 4;
 };
 
 constexpr float kLazySlack = 8.f;  // log2 units the reference max may trail the true max
 
 // LDS of the walk: stage buffers by slot (group g's stage at offset g * kStage of each
-// array) and the V^T operands of each group's current stage.  Five separate objects, so the
-// compiler can tell reads of one from loads into another.
+// array) and the max / sum records of the final merge.  Separate objects, so the compiler
+// can tell reads of one from loads into another.
 template <int D>
 struct PPSmem {
   uint8_t* sk0;
   uint8_t* sk1;
   uint8_t* sv0;
   uint8_t* sv1;
-  uint8_t* svt;
+  uint8_t* sml;
 };
 
 // One Q tile (work item `work` of the tiles at qtiles) walked by the workgroup.  R64: the
@@ -469,15 +470,14 @@ __device__ __forceinline__ void pp_walk(const FwdParams& p, const CONST_AS int32
   uint8_t* const sk1 = sm.sk1;
   uint8_t* const sv0 = sm.sv0;
   uint8_t* const sv1 = sm.sv1;
-  uint8_t* const svt = sm.svt;
-  static_assert(4 * C::kDB * 1024 == C::kStage, "one 1 KB operand per 16 keys x 32 d");
-  static_assert(2 * C::kRecord <= 2 * C::kStage && 6 * 2 * 64 * 4 <= 2 * C::kStage, "merge records fit");
+  uint8_t* const sml = sm.sml;
+  static_assert(2 * C::kRecord <= 2 * C::kStage, "two O^T records fit in a stage slot array");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;                  // stage group
-  const int wr = wave & 3;                    // the page of each stage this wave loads and transposes
+  const int wr = wave & 3;                    // the page of each stage this wave loads
   const int rg = R64 ? (wr & 1) : wr;         // row group
   const int kh = R64 ? (wr >> 1) : 0;         // key half of the stage (64-row tiles)
   const int hh = lane >> 5;
@@ -642,49 +642,32 @@ __device__ __forceinline__ void pp_walk(const FwdParams& p, const CONST_AS int32
     }
   }
 
-  // Transposed V: wave wr turns the 16 keys of chunk wr of the group's V stage at vb into the
-  // V^T operands (chunk wr, d block db) of the next matrix phase, each stored as 64 lanes x
-  // 16 bytes, so that phase reads every operand with one conflict-free 16-byte load.
-  const uint32_t opofs = goff + lane * 16;
-  // first V^T operand of this wave's keys: chunks 2 kh, 2 kh + 1 of a 64-row tile's stage
-  const uint32_t vtofs = opofs + 2 * kh * C::kDB * 1024;
-  struct VtOps {
-    bf16x8 op[C::kDB];
-  };
-  auto transpose_read = [&](const uint8_t* vb) __attribute__((always_inline)) {
-    VtOps tv;
+  // V^T operand (16-key chunk c of the wave's keys, d block db), read straight from the V
+  // stage with two transposing reads: per-lane offsets with the wave's key half folded in.
+  uint32_t vofa_w[C::kDB], vofb_w[C::kDB];
 #pragma unroll
-    for (int db = 0; db < C::kDB; ++db) {
-      const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(vb + vofa[db] + wr * 16 * C::kRowBytes));
-      const bf16x4 vq = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(vb + vofb[db] + wr * 16 * C::kRowBytes));
-      tv.op[db] = bf16x8{va[0], va[1], va[2], va[3], vq[0], vq[1], vq[2], vq[3]};
-    }
-    return tv;
-  };
-  auto transpose_write = [&](const VtOps& tv) __attribute__((always_inline)) {
-#pragma unroll
-    for (int db = 0; db < C::kDB; ++db) *reinterpret_cast<bf16x8*>(svt + opofs + (wr * C::kDB + db) * 1024) = tv.op[db];
-  };
+  for (int db = 0; db < C::kDB; ++db) {
+    vofa_w[db] = vofa[db] + (R64 ? 2 * kh * 16 * C::kRowBytes : 0);
+    vofb_w[db] = vofb[db] + (R64 ? 2 * kh * 16 * C::kRowBytes : 0);
+  }
 
-  // Matrix phase: O^T += V^T P^T over the staged V^T operands (PV), then S^T = K Q^T over the
-  // K stage at kb (QK).  The products run as one list (PV: 16-key chunk c, d block db; QK:
+  // Matrix phase: O^T += V^T P^T over the V stage at vb (PV), then S^T = K Q^T over the K
+  // stage at kb (QK).  The products run as one list (PV: 16-key chunk c, d block db; QK:
   // k-step s, key block j) whose operands are read kLead products ahead of their use, so
   // the matrix core does not stall on LDS latency between products.  Without ACT (a wave
   // with no valid rows) the phase issues only the loads.
-  constexpr int kNPV = 2 * JB * C::kDB, kNQK = JB * C::kDS, kLead = 4;
-  auto mphase = [&](const uint8_t* kb, auto pv_tag, auto qk_tag, const PageLoad* ldk, uint8_t* kdst, const PageLoad* ldv,
-                    uint8_t* vdst, auto act_tag) __attribute__((always_inline)) {
+  constexpr int kNPV = 2 * JB * C::kDB, kNQK = JB * C::kDS, kLead = 2;
+  auto mphase = [&](const uint8_t* kb, const uint8_t* vb, auto pv_tag, auto qk_tag, const PageLoad* ldk, uint8_t* kdst,
+                    auto act_tag) __attribute__((always_inline)) {
     constexpr bool PV = decltype(pv_tag)::value, QK = decltype(qk_tag)::value, ACT = decltype(act_tag)::value;
     constexpr int n0 = PV ? 0 : kNPV;
     constexpr int n1 = QK ? kNPV + kNQK : kNPV;
-    constexpr int kSpread = (n1 - n0) / (2 * C::kInst);  // one load before every kSpread-th product
+    constexpr int kSpread = (n1 - n0) / C::kInst;  // one load before every kSpread-th product
     static_assert(kSpread >= 1, "a product per load");
     if constexpr (!ACT) {
       if (ldk) {
 #pragma unroll
         for (int n = 0; n < C::kInst; ++n) fire(*ldk, krsrc, kdst, n);
-#pragma unroll
-        for (int n = 0; n < C::kInst; ++n) fire(*ldv, vrsrc, vdst, n);
       }
       return;
     }
@@ -710,7 +693,10 @@ __device__ __forceinline__ void pp_walk(const FwdParams& p, const CONST_AS int32
     auto load = [&](auto it) __attribute__((always_inline)) {
       constexpr int i = decltype(it)::value;
       if constexpr (i < kNPV) {
-        ring[(i - n0) % (kLead + 1)] = *reinterpret_cast<const bf16x8*>(svt + vtofs + i * 1024);
+        constexpr int c = i / C::kDB, db = i % C::kDB;
+        const bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(vb + vofa_w[db] + c * 16 * C::kRowBytes));
+        const bf16x4 vq = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(vb + vofb_w[db] + c * 16 * C::kRowBytes));
+        ring[(i - n0) % (kLead + 1)] = bf16x8{va[0], va[1], va[2], va[3], vq[0], vq[1], vq[2], vq[3]};
       } else {
         constexpr int s = (i - kNPV) / JB, j = (i - kNPV) % JB;
         ring[(i - n0) % (kLead + 1)] = *reinterpret_cast<const bf16x8*>(kb + kofs[s] + j * 32 * C::kRowBytes);
@@ -734,21 +720,22 @@ __device__ __forceinline__ void pp_walk(const FwdParams& p, const CONST_AS int32
         constexpr int tt = (i - n0) / kSpread;
         if constexpr (tt < C::kInst) {
           if (ldk) fire(*ldk, krsrc, kdst, tt);
-        } else if constexpr (tt < 2 * C::kInst) {
-          if (ldv) fire(*ldv, vrsrc, vdst, tt - C::kInst);
         }
       }
       if constexpr (i + kLead < n1) load(IntTag<i + kLead>{});
       mma(it);
     });
     // keep the order: operand reads kLead products ahead of the MFMAs, loads spread out
-    __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
+    static_for<n0, (n0 + kLead < n1 ? n0 + kLead : n1)>([&](auto it) __attribute__((always_inline)) {
+      constexpr int i = decltype(it)::value;
+      __builtin_amdgcn_sched_group_barrier(0x100, i < kNPV ? 2 : 1, 0);
+    });
     static_for<n0, n1>([&](auto it) __attribute__((always_inline)) {
       constexpr int i = decltype(it)::value;
-      if constexpr ((i - n0) % kSpread == 0 && (i - n0) / kSpread < 2 * C::kInst) {
+      if constexpr ((i - n0) % kSpread == 0 && (i - n0) / kSpread < C::kInst) {
         if (ldk) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
-      if constexpr (i + kLead < n1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if constexpr (i + kLead < n1) __builtin_amdgcn_sched_group_barrier(0x100, i + kLead < kNPV ? 2 : 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     });
     // the products stay in this phase (see pin_vector_phase)
@@ -843,13 +830,12 @@ __device__ __forceinline__ void pp_walk(const FwdParams& p, const CONST_AS int32
     pin_vector_phase();
   };
 
-  // Load schedule of local stage j: matrix phase j issues K(j + 1) and V(j + 1), spread over
-  // its products (K(j + 1)'s slot held K(j - 1), read in matrix phase j - 1; V(j + 1)'s held
-  // V(j - 1), transposed in vector phase j - 1).  Matrix phase j ends by waiting for V(j),
-  // vector phase j for K(j + 1).  Vector phases issue no loads: their waves are the busier
-  // ones, and a wave stalls while a load waits for the CU's memory pipeline.  Page entries of
-  // stage j + 3 are loaded in vector phase j, after its LDS work, so that no LDS wait ever
-  // covers a scalar load in flight.
+  // Load schedule of local stage j: matrix phase j issues K(j + 1), spread over its products
+  // (its slot held K(j - 1), read in matrix phase j - 1); vector phase j issues V(j + 1) at
+  // its start (its slot held V(j - 1), read by the P.V products of matrix phase j, which the
+  // barrier between the two phases has closed).  Vector phase j ends by waiting for K(j + 1),
+  // and with it for V(j), issued before it.  Page entries of stage j + 3 are loaded in vector
+  // phase j, where no LDS wait can cover the scalar load.
   if (ns > 0) {
     SVec<4> x0 = entries(0), x1 = entries(1), x2 = entries(2);  // raw entries of stages j, j + 1, j + 2
     issue(mine(x0, 0), krsrc, p.k_sn_bytes, ld_vk, sk0);
@@ -862,45 +848,47 @@ __device__ __forceinline__ void pp_walk(const FwdParams& p, const CONST_AS int32
       constexpr bool ACT = decltype(act_tag)::value;
       // matrix phase: P.V of the previous stage (if PV), S of the stage in kbuf (if QK), loads
       // of stage jn (entry word ent) into kdst / vdst
-      auto mph = [&](auto pv_tag, auto qk_tag, const uint8_t* kbuf, int ent, uint8_t* kdst, uint8_t* vdst)
+      auto mph = [&](auto pv_tag, auto qk_tag, const uint8_t* kbuf, const uint8_t* vbuf, int ent, uint8_t* kdst)
                      __attribute__((always_inline)) {
         const PageLoad lk = prep(ent, p.k_sn_bytes, ld_vk);
-        const PageLoad lv = prep(ent, p.v_sn_bytes, ld_vv);
-        mphase(kbuf, pv_tag, qk_tag, &lk, kdst, &lv, vdst, act_tag);
-        wait_vmcnt<2 * C::kInst>();  // V of the phase's own stage landed
+        mphase(kbuf, vbuf, pv_tag, qk_tag, &lk, kdst, act_tag);
         bar();
       };
-      // vector phase of stage j: V(j) transposed from vbuf, entries of stage j + 3 loaded,
-      // softmax with raw entries ej
-      auto vph = [&](int j, const SVec<4>& ej, const uint8_t* vbuf) __attribute__((always_inline)) {
-        transpose_write(transpose_read(vbuf));
+      // vector phase of stage j: V of stage j + 1 (entry word ent) loaded into vdst, entries of
+      // stage j + 3 loaded, softmax with raw entries ej
+      auto vph = [&](int j, const SVec<4>& ej, int ent, uint8_t* vdst) __attribute__((always_inline)) {
+        issue(ent, vrsrc, p.v_sn_bytes, ld_vv, vdst);
         __builtin_amdgcn_sched_barrier(0);
         const SVec<4> next = entries(j + 3);
         if constexpr (ACT) softmax(ej, j);
-        wait_vmcnt<C::kInst>();  // K of the next stage landed
+        wait_vmcnt<C::kInst>();  // K of the next stage landed (V of this one was issued before it)
         bar();
         return next;
       };
-      mph(BoolTag<false>{}, BoolTag<true>{}, sk0, mine(x1, 1), sk1, sv1);
-      const SVec<4> x3 = vph(0, x0, sv0);
+      mph(BoolTag<false>{}, BoolTag<true>{}, sk0, sv0, mine(x1, 1), sk1);
+      const SVec<4> x3 = vph(0, x0, mine(x1, 1), sv1);
       x0 = x1;
       x1 = x2;
       x2 = x3;
       int j = 1;
       for (; j + 1 < my_n; j += 2) {
-        mph(BoolTag<true>{}, BoolTag<true>{}, sk1, mine(x1, j + 1), sk0, sv0);  // P.V of j - 1, S of j (odd)
-        const SVec<4> x3n = vph(j, x0, sv1);
-        mph(BoolTag<true>{}, BoolTag<true>{}, sk0, mine(x2, j + 2), sk1, sv1);  // P.V of j, S of j + 1 (even)
-        const SVec<4> x4 = vph(j + 1, x1, sv0);
+        mph(BoolTag<true>{}, BoolTag<true>{}, sk1, sv0, mine(x1, j + 1), sk0);  // P.V of j - 1, S of j (odd)
+        const SVec<4> x3n = vph(j, x0, mine(x1, j + 1), sv0);
+        mph(BoolTag<true>{}, BoolTag<true>{}, sk0, sv1, mine(x2, j + 2), sk1);  // P.V of j, S of j + 1 (even)
+        const SVec<4> x4 = vph(j + 1, x1, mine(x2, j + 2), sv1);
         x0 = x2;
         x1 = x3n;
         x2 = x4;
       }
       if (j < my_n) {
-        mph(BoolTag<true>{}, BoolTag<true>{}, sk1, mine(x1, j + 1), sk0, sv0);
-        vph(j, x0, sv1);
+        mph(BoolTag<true>{}, BoolTag<true>{}, sk1, sv0, mine(x1, j + 1), sk0);
+        vph(j, x0, mine(x1, j + 1), sv0);
       }
-      mphase(sk0, BoolTag<true>{}, BoolTag<false>{}, nullptr, nullptr, nullptr, nullptr, act_tag);  // P.V of the last stage
+      // P.V of the last stage, my_n - 1, whose V is in slot (my_n - 1) & 1
+      if (my_n & 1)
+        mphase(sk0, sv0, BoolTag<true>{}, BoolTag<false>{}, nullptr, nullptr, act_tag);
+      else
+        mphase(sk0, sv1, BoolTag<true>{}, BoolTag<false>{}, nullptr, nullptr, act_tag);
       bar();
     };
     if (my_n > 0) {
@@ -920,7 +908,7 @@ __device__ __forceinline__ void pp_walk(const FwdParams& p, const CONST_AS int32
   // ---- finish: combine lane halves, merge the states of each row group, write O and LSE ----
   // States: one per group (128-row tiles), one per (group, key half) (64-row tiles).  Every
   // state but (group 0, key half 0) goes to LDS as a record -- O^T in one of the four stage
-  // arrays, max and sum in the V^T array -- and that wave combines them.
+  // arrays, max and sum in the record array -- and that wave combines them.
   float l_tot = xor32_sum(l_run);
   constexpr int kStates = R64 ? 4 : 2;                 // states per row group
   const int sidx = R64 ? (2 * grp + kh) : grp;         // this wave's state
@@ -929,7 +917,7 @@ __device__ __forceinline__ void pp_walk(const FwdParams& p, const CONST_AS int32
     const int rec = rg * (kStates - 1) + sidx - 1;     // 0 .. 3 (128-row) or 0 .. 5 (64-row)
     uint8_t* arr = (rec >> 1) == 0 ? sk0 : ((rec >> 1) == 1 ? sk1 : ((rec >> 1) == 2 ? sv0 : sv1));
     float* ob = reinterpret_cast<float*>(arr + (rec & 1) * C::kRecord);
-    float* mlb = reinterpret_cast<float*>(svt) + rec * 128;
+    float* mlb = reinterpret_cast<float*>(sml) + rec * 128;
 #pragma unroll
     for (int db = 0; db < C::kDB; ++db)
 #pragma unroll
@@ -941,7 +929,7 @@ __device__ __forceinline__ void pp_walk(const FwdParams& p, const CONST_AS int32
   if (sidx != 0) return;
   float mm = mref;
 #pragma unroll
-  for (int s = 1; s < kStates; ++s) mm = fmaxf(mm, reinterpret_cast<const float*>(svt)[(rg * (kStates - 1) + s - 1) * 128 + lane]);
+  for (int s = 1; s < kStates; ++s) mm = fmaxf(mm, reinterpret_cast<const float*>(sml)[(rg * (kStates - 1) + s - 1) * 128 + lane]);
   const float mu = (mm == kNegInf) ? 0.f : mm;
   {
     const float a0 = __builtin_amdgcn_exp2f(mref - mu);
@@ -954,7 +942,7 @@ __device__ __forceinline__ void pp_walk(const FwdParams& p, const CONST_AS int32
     const int rec = rg * (kStates - 1) + s - 1;
     const uint8_t* arr = (rec >> 1) == 0 ? sk0 : ((rec >> 1) == 1 ? sk1 : ((rec >> 1) == 2 ? sv0 : sv1));
     const float* ob = reinterpret_cast<const float*>(arr + (rec & 1) * C::kRecord);
-    const float* mlb = reinterpret_cast<const float*>(svt) + rec * 128;
+    const float* mlb = reinterpret_cast<const float*>(sml) + rec * 128;
     const float a1 = __builtin_amdgcn_exp2f(mlb[lane] - mu);
 #pragma unroll
     for (int db = 0; db < C::kDB; ++db)
@@ -1024,8 +1012,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   __shared__ __attribute__((aligned(1024))) uint8_t sk1[2 * PPCfg<D>::kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t sv0[2 * PPCfg<D>::kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t sv1[2 * PPCfg<D>::kStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t svt[2 * PPCfg<D>::kStage];
-  const PPSmem<D> sm{sk0, sk1, sv0, sv1, svt};
+  __shared__ __attribute__((aligned(1024))) uint8_t sml[PPCfg<D>::kMlBytes];
+  const PPSmem<D> sm{sk0, sk1, sv0, sv1, sml};
   const int x = blockIdx.x & 7, i = blockIdx.x >> 3;
   const XcdList l = xcd_list(x, p.n_qtiles, p.B * p.Hq);
   if (i >= l.count) return;  // the grid covers the longest XCD list
@@ -1042,8 +1030,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
   __shared__ __attribute__((aligned(1024))) uint8_t sk1[2 * PPCfg<D>::kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t sv0[2 * PPCfg<D>::kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t sv1[2 * PPCfg<D>::kStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t svt[2 * PPCfg<D>::kStage];
-  const PPSmem<D> sm{sk0, sk1, sv0, sv1, svt};
+  __shared__ __attribute__((aligned(1024))) uint8_t sml[PPCfg<D>::kMlBytes];
+  const PPSmem<D> sm{sk0, sk1, sv0, sv1, sml};
   const int x = blockIdx.x & 7, i = blockIdx.x >> 3, BH = p.B * p.Hq;
   const XcdList a = xcd_list(x, p.n_qtiles, BH);
   if (i < a.count) {
