@@ -148,6 +148,24 @@ def cpu_baseline_chunks(w, chunk, topk, gpu_chunks):
                       f"same chunks as the GPU: {same}"}
 
 
+def gpu_chunk_select(w, chunk, topk):
+    """Selection of the chunk-indexed workloads (chunk summaries scored by one indexing query
+    per KV group, top-k) computed on the GPU by bsattn_chunk_select from the drawn Q and K;
+    the GPU tests check that call against the float64 oracle."""
+    import torch
+    import block_sparse_attention_fwd_amd as bs
+
+    def to_dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+
+    q, k = to_dev(w.q), to_dev(w.k)
+    _, chunks = bs.chunk_select(q, k, w.Hkv, chunk, topk)
+    torch.cuda.synchronize()
+    sel = chunks.cpu().numpy().astype(np.int32).reshape(w.B * w.Hkv, topk)
+    del q, k
+    return sel
+
+
 def bench_bwd(args, w, plan, st, t_plan, dev):
     """One step = one bsattn_bwd call (D, then dK/dV, then dQ) on resident inputs, with O and
     LSE from one forward call before the timed region."""
@@ -272,7 +290,7 @@ def bench_decode(args, dev):
 
     t0 = time.perf_counter()
     w = make_chunk_gqa("chunk-gqa-decode-b4-h64kv8-262144-d128", 5, B=4, Hq=64, Hkv=8, d=128, Nk=262144, Nq=1,
-                       chunk=64, topk=2048)
+                       chunk=64, topk=2048, chunk_select=gpu_chunk_select)
     log(f"[bench] decode workload generated in {time.perf_counter() - t0:.1f} s")
     plan = bs.Plan.from_workload(w).upload()
     st = plan.stats
@@ -395,7 +413,7 @@ def main():
         bench_decode(args, dev)
         return
     t0 = time.perf_counter()
-    w = make(args.workload)
+    w = make(args.workload, chunk_select=gpu_chunk_select)
     log(f"[bench] workload {w.name}: inputs generated in {time.perf_counter() - t0:.1f} s")
 
     if args.chunk_select:

@@ -24,6 +24,7 @@ import torch
 import block_sparse_attention_fwd_amd as bs
 from oracle.attention import masked_attention_bwd_w, masked_attention_w
 from workloads.configs import make, make_random, make_partitions, draw_dout
+from tests.oracle_select import oracle_chunk_select
 
 pytestmark = pytest.mark.gpu
 
@@ -218,7 +219,7 @@ def test_bwd_chunk_gqa_full_size_sampled():
     # chunk-indexed GQA prefill at full size (4 x 262,144 keys, 64 query heads in 8 KV groups,
     # causal): dQ of sampled query rows against the oracle (each reaches its group's 131,072
     # selected keys), and exact zeros in dK/dV for chunks that a group does not select
-    w = make(5)
+    w = make(5, chunk_select=oracle_chunk_select)
     _say(f"[gpu-bwd] chunk GQA full size: B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Nk={w.Nk} causal={w.causal}")
     dq, dk, dv, plan = run_gpu_bwd(w)
     assert np.all(np.isfinite(dq)) and np.all(np.isfinite(dk)) and np.all(np.isfinite(dv))

@@ -72,7 +72,9 @@ def test_chunk_select_small(d, Nk, chunk, topk, Hq, Hkv):
 def test_chunk_select_long_prefill_sampled():
     # the chunk-indexed GQA prefill shape: 4 x 262,144 keys, 8 KV groups of 8 query heads,
     # 64-token chunks, top-2048; two (batch, group) units checked against the oracle
-    w = make_chunk_gqa("chunk-gqa", 5, B=4, Hq=64, Hkv=8, d=128, Nk=262144, Nq=2048, chunk=64, topk=2048)
+    # (only the drawn Q and K are used here: a placeholder selection spares the oracle's)
+    w = make_chunk_gqa("chunk-gqa", 5, B=4, Hq=64, Hkv=8, d=128, Nk=262144, Nq=2048, chunk=64, topk=2048,
+                       chunk_select=lambda w_, c, t: np.tile(np.arange(t, dtype=np.int32), (w_.B * w_.Hkv, 1)))
     summ, chunks = bs.chunk_select(_dev(w.q), _dev(w.k), w.Hkv, 64, 2048)
     torch.cuda.synchronize()
     summ = summ.cpu().numpy()

@@ -12,6 +12,7 @@ import torch
 import block_sparse_attention_fwd_amd as bs
 from oracle.attention import masked_attention_w
 from workloads.configs import make_chunk_gqa, make_random
+from tests.oracle_select import oracle_chunk_select
 
 pytestmark = pytest.mark.gpu
 
@@ -50,7 +51,8 @@ def check_decode(w, label):
 
 @pytest.mark.parametrize("Nq,Hq,Hkv,d", [(1, 16, 2, 128), (4, 16, 2, 128), (2, 8, 8, 128), (1, 8, 1, 64)])
 def test_decode_chunk_gqa(Nq, Hq, Hkv, d):
-    w = make_chunk_gqa("decode", 300 + Nq + d, B=2, Hq=Hq, Hkv=Hkv, d=d, Nk=64 * 150 + 64, Nq=Nq, chunk=64, topk=40)
+    w = make_chunk_gqa("decode", 300 + Nq + d, B=2, Hq=Hq, Hkv=Hkv, d=d, Nk=64 * 150 + 64, Nq=Nq, chunk=64, topk=40,
+                       chunk_select=oracle_chunk_select)
     check_decode(w, f"chunk-gqa Nq={Nq} Hq={Hq} Hkv={Hkv} d={d}")
 
 
@@ -64,7 +66,8 @@ def test_decode_random_small_blocks(seed, perm, causal):
 
 
 def test_decode_matches_forward_path():
-    w = make_chunk_gqa("decode", 320, B=1, Hq=16, Hkv=2, d=128, Nk=64 * 300, Nq=2, chunk=64, topk=100)
+    w = make_chunk_gqa("decode", 320, B=1, Hq=16, Hkv=2, d=128, Nk=64 * 300, Nq=2, chunk=64, topk=100,
+                       chunk_select=oracle_chunk_select)
     plan = bs.Plan.from_workload(w).upload()
     q, k, v = _dev(w.q), _dev(w.k), _dev(w.v)
     o1, l1 = plan.fwd(q, k, v, scale=w.scale)

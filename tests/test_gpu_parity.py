@@ -17,6 +17,7 @@ import block_sparse_attention_fwd_amd as bs
 from oracle.attention import masked_attention_w
 from oracle.planner import build_plan_w
 from workloads.configs import make, make_random, make_chunk_gqa
+from tests.oracle_select import oracle_chunk_select
 
 pytestmark = pytest.mark.gpu
 
@@ -225,10 +226,11 @@ def test_partitions_full_size_sampled():
 
 def test_chunk_gqa_scaled_full():
     # same recipe as the long-context GQA workload, scaled down so every output is compared
-    w = make_chunk_gqa("chunk-gqa-small", 5, B=2, Hq=8, Hkv=2, d=128, Nk=64 * 96, Nq=256, chunk=64, topk=40)
+    w = make_chunk_gqa("chunk-gqa-small", 5, B=2, Hq=8, Hkv=2, d=128, Nk=64 * 96, Nq=256, chunk=64, topk=40,
+                       chunk_select=oracle_chunk_select)
     check_full(w, "chunk-gqa-small")
 
 
 def test_chunk_gqa_full_size_sampled():
-    w = make(5)
+    w = make(5, chunk_select=oracle_chunk_select)
     check_sampled(w, "chunk-gqa", heads=[(0, 0), (1, 9), (3, 63)], n_rows=64, extra_rows=[0, 2047])

@@ -16,6 +16,7 @@ import torch
 import block_sparse_attention_fwd_amd as bs
 from oracle.attention import masked_attention_w
 from workloads.configs import make_random, make_chunk_gqa
+from tests.oracle_select import oracle_chunk_select
 
 pytestmark = pytest.mark.gpu
 
@@ -55,8 +56,10 @@ def test_device_update_equals_host_plan(seed, perm, causal, decode, many_rows):
     # with 5,000 chunks per sequence: 20,000 transposed lists) are scanned over the whole chip.
     if decode:
         nch = 5000 if many_rows else 120
-        w1 = make_chunk_gqa("u1", seed, B=2, Hq=16, Hkv=2, d=128, Nk=64 * nch, Nq=1, chunk=64, topk=30)
-        w2 = make_chunk_gqa("u2", seed + 50, B=2, Hq=16, Hkv=2, d=128, Nk=64 * nch, Nq=1, chunk=64, topk=30)
+        w1 = make_chunk_gqa("u1", seed, B=2, Hq=16, Hkv=2, d=128, Nk=64 * nch, Nq=1, chunk=64, topk=30,
+                            chunk_select=oracle_chunk_select)
+        w2 = make_chunk_gqa("u2", seed + 50, B=2, Hq=16, Hkv=2, d=128, Nk=64 * nch, Nq=1, chunk=64, topk=30,
+                            chunk_select=oracle_chunk_select)
         w2.q, w2.k, w2.v = w1.q, w1.k, w1.v  # same tensors, the second seed's selection
     else:
         nq, mq = (3000, 8) if many_rows else (400, 130)
@@ -135,7 +138,8 @@ def test_device_update_status_bits():
 def test_chunk_select_to_decode_on_device():
     # the whole step on the device: chunk selection -> page lists -> head-stacked decode, equal
     # to the host plan built from the same chunks
-    w = make_chunk_gqa("pipe", 420, B=2, Hq=16, Hkv=2, d=128, Nk=64 * 200, Nq=1, chunk=64, topk=50)
+    w = make_chunk_gqa("pipe", 420, B=2, Hq=16, Hkv=2, d=128, Nk=64 * 200, Nq=1, chunk=64, topk=50,
+                       chunk_select=oracle_chunk_select)
     q, k, v = _dev(w.q), _dev(w.k), _dev(w.v)
     plan = bs.Plan.from_workload(w).upload()
     _, chunks = bs.chunk_select(q, k, w.Hkv, 64, 50)

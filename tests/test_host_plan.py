@@ -13,6 +13,7 @@ import pytest
 import block_sparse_attention_fwd_amd as bs
 from oracle.planner import build_plan_w, build_bwd_plan_w
 from workloads.configs import make, make_random, make_chunk_gqa
+from tests.oracle_select import oracle_chunk_select
 
 
 def _compare(w, flags=0):
@@ -46,7 +47,8 @@ def test_configs_bit_exact(cfg):
 
 
 def test_chunk_gqa_scaled_bit_exact():
-    w = make_chunk_gqa("small", 5, B=2, Hq=8, Hkv=2, d=64, Nk=64 * 300, Nq=512, chunk=64, topk=120)
+    w = make_chunk_gqa("small", 5, B=2, Hq=8, Hkv=2, d=64, Nk=64 * 300, Nq=512, chunk=64, topk=120,
+                       chunk_select=oracle_chunk_select)
     st = _compare(w)
     assert st["useful"] < 2 * 8 * 512 * 120 * 64  # causal exclusions removed
 
@@ -204,7 +206,8 @@ def test_block_order_hint_validates_and_keeps_canonical_arrays():
 
 
 def test_decode_geometry_and_unsupported_plans():
-    w = make_chunk_gqa("decode", 7, B=2, Hq=16, Hkv=2, d=128, Nk=64 * 150, Nq=1, chunk=64, topk=40)
+    w = make_chunk_gqa("decode", 7, B=2, Hq=16, Hkv=2, d=128, Nk=64 * 150, Nq=1, chunk=64, topk=40,
+                       chunk_select=oracle_chunk_select)
     p = bs.Plan.from_workload(w)
     assert bs.bsattn_decode_workspace_bytes(p.handle) > 0
     big = make_random(8, B=1, Hq=8, Hkv=1, Nq=100, Nk=100, d=64, max_qblock=20, sel_mode="kv", with_tensors=False)
@@ -236,7 +239,8 @@ def test_decode_noalloc_limits():
     with pytest.raises(bs.BsattnError) as e:
         bs.bsattn_fwd_decode_noalloc(pb.handle, 16, 16, 16, 16, 16, 0.125, 0)
     assert e.value.status == 4
-    w = make_chunk_gqa("decode", 7, B=2, Hq=16, Hkv=2, d=128, Nk=64 * 150, Nq=1, chunk=64, topk=40)
+    w = make_chunk_gqa("decode", 7, B=2, Hq=16, Hkv=2, d=128, Nk=64 * 150, Nq=1, chunk=64, topk=40,
+                       chunk_select=oracle_chunk_select)
     p = bs.Plan.from_workload(w)
     assert bs.bsattn_decode_workspace_bytes(p.handle) <= 16 << 20
     with pytest.raises(bs.BsattnError) as e:

@@ -4,6 +4,7 @@ import pytest
 import torch
 
 import workloads.configs as wc
+from tests.oracle_select import oracle_chunk_select
 
 
 def test_bf16_rounding_matches_torch():
@@ -43,9 +44,14 @@ def test_partition_workload_shape():
         assert ksz[sel].sum() <= 11340 and len(sel) > 0
 
 
-def test_chunk_topk_selection_small():
-    # a scaled-down long-context GQA case: the selection is the top-k of a full sort
-    w = wc.make_chunk_gqa("small", 9, B=2, Hq=8, Hkv=2, d=16, Nk=64 * 40, Nq=128, chunk=64, topk=10)
+def test_chunk_gqa_selection_wiring():
+    # a scaled-down long-context GQA case: the generator asks its caller for the selection
+    # (here the oracle's) and files row b * Hkv + g under unit (b, g); that row is the top-k
+    # of a full sort of the chunk scores
+    with pytest.raises(ValueError):
+        wc.make(5, with_tensors=True)
+    w = wc.make_chunk_gqa("small", 9, B=2, Hq=8, Hkv=2, d=16, Nk=64 * 40, Nq=128, chunk=64, topk=10,
+                          chunk_select=oracle_chunk_select)
     assert w.sel_nb == 2 and w.sel_nh == 2 and w.causal and w.q_pos0 == 64 * 40 - 128
     kf = wc.f32_from_bf16_bits(w.k).astype(np.float64)
     qf = wc.f32_from_bf16_bits(w.q).astype(np.float64)

@@ -12,6 +12,7 @@ import torch
 import block_sparse_attention_fwd_amd as bs
 from oracle.attention import masked_attention_w
 from workloads.configs import make_chunk_gqa
+from tests.oracle_select import oracle_chunk_select
 
 pytestmark = pytest.mark.gpu
 
@@ -43,8 +44,10 @@ def _decode_both(w):
 
 def test_noalloc_decode_two_calls():
     cases = [
-        make_chunk_gqa("decode-a", 401, B=2, Hq=16, Hkv=2, d=128, Nk=64 * 300, Nq=2, chunk=64, topk=120),
-        make_chunk_gqa("decode-b", 402, B=1, Hq=8, Hkv=1, d=128, Nk=64 * 90, Nq=1, chunk=64, topk=30),
+        make_chunk_gqa("decode-a", 401, B=2, Hq=16, Hkv=2, d=128, Nk=64 * 300, Nq=2, chunk=64, topk=120,
+                       chunk_select=oracle_chunk_select),
+        make_chunk_gqa("decode-b", 402, B=1, Hq=8, Hkv=1, d=128, Nk=64 * 90, Nq=1, chunk=64, topk=30,
+                       chunk_select=oracle_chunk_select),
     ]
     for w in cases:
         print(f"[noalloc] {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Nk={w.Nk}", flush=True)

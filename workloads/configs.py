@@ -14,7 +14,9 @@ structure first (masks, partitions, selections), then Q, K, V, each drawn as
 float32 N(0, 1) over the whole tensor in C order and rounded to bf16 with
 round-to-nearest-even.  The only data-dependent structure is the chunk
 selection of the long-context GQA workload, which is derived from the drawn Q
-and K after they exist (chunk summaries, CISA abstract sentences 3-5).
+and K after they exist (chunk summaries, CISA abstract sentences 3-5) by a
+selection function the caller passes in: this module holds no arithmetic of the
+method itself.
 """
 from __future__ import annotations
 
@@ -272,33 +274,18 @@ def make_partitions(name, seed, N, H, d, lo=16, hi=300, key_frac=0.15, B=1, with
     return w
 
 
-def chunk_topk_selection(q: np.ndarray, k: np.ndarray, chunk: int, topk: int, Hq: int, Hkv: int) -> np.ndarray:
-    """Per (batch, KV group): score each KV chunk by the dot product of its mean key
-    (a compact key summary) with one indexing query -- the mean over the group's
-    query heads of the last query row -- and keep the ``topk`` best chunks (ties to the
-    lower chunk index).  Returns int32 [B * Hkv, topk] sorted ascending.
-    Values are bf16 bit patterns widened to float64."""
-    B, Nk = k.shape[0], k.shape[1]
-    nchunks = Nk // chunk
-    grp = Hq // Hkv
-    out = np.empty((B * Hkv, topk), dtype=np.int32)
-    for b in range(B):
-        qlast = f32_from_bf16_bits(q[b, -1]).astype(np.float64)  # [Hq, d]
-        for g in range(Hkv):
-            iq = qlast[g * grp:(g + 1) * grp].mean(axis=0)
-            kg = f32_from_bf16_bits(k[b, :nchunks * chunk, g]).astype(np.float64)
-            summ = kg.reshape(nchunks, chunk, -1).mean(axis=1)
-            score = summ @ iq
-            order = np.lexsort((np.arange(nchunks), -score))
-            out[b * Hkv + g] = np.sort(order[:topk]).astype(np.int32)
-    return out
-
-
-def make_chunk_gqa(name, seed, B, Hq, Hkv, d, Nk, Nq, chunk, topk, causal=True, with_tensors=True) -> Workload:
+def make_chunk_gqa(name, seed, B, Hq, Hkv, d, Nk, Nq, chunk, topk, *, chunk_select, causal=True,
+                   with_tensors=True) -> Workload:
     """Long-context GQA prefill over selected KV chunks.  The queries are the last Nq
     positions of an Nk-token sequence (query i sits at absolute position Nk - Nq + i);
     one Q block holds all of them (QShare) and each (batch, KV group) unit selects the
-    same chunk set for all its query heads."""
+    same chunk set for all its query heads.
+
+    The selection is computed from the drawn Q and K by ``chunk_select(w, chunk, topk)``,
+    which returns int32 [B * Hkv, topk] (ascending chunk ids per (batch, KV group)).  The
+    chunk scoring is part of the method (CISA abstract, sentences 3-5), so this module only
+    draws the inputs and the caller brings the selection: the tests use the float64 oracle's,
+    the benchmark the GPU's (which the tests check against the oracle)."""
     rng = np.random.default_rng(seed)
     qoffs = np.array([0, Nq], dtype=np.int32)
     koffs = uniform_layout(Nk, chunk)
@@ -309,14 +296,17 @@ def make_chunk_gqa(name, seed, B, Hq, Hkv, d, Nk, Nq, chunk, topk, causal=True, 
     if not with_tensors:
         raise ValueError("the chunk selection is derived from Q and K; tensors are required")
     _tensors(w, rng)
-    sel = chunk_topk_selection(w.q, w.k, chunk, topk, Hq, Hkv)
+    sel = np.asarray(chunk_select(w, chunk, topk), dtype=np.int32)
+    if sel.shape != (B * Hkv, topk):
+        raise ValueError(f"chunk_select returned shape {sel.shape}, expected {(B * Hkv, topk)}")
     w.sel_row_ptr = (np.arange(B * Hkv + 1, dtype=np.int64) * topk).astype(np.int32)
     w.sel_kblk = sel.reshape(-1)
     return w
 
 
-def make(cfg: int, seed: Optional[int] = None, with_tensors: bool = True) -> Workload:
-    """The five benchmark workloads at full size; seed defaults to the config number."""
+def make(cfg: int, seed: Optional[int] = None, with_tensors: bool = True, chunk_select=None) -> Workload:
+    """The five benchmark workloads at full size; seed defaults to the config number.
+    Workload 5 needs ``chunk_select`` (see make_chunk_gqa)."""
     s = cfg if seed is None else seed
     name = CONFIG_NAMES[cfg]
     if cfg == 1:
@@ -328,8 +318,10 @@ def make(cfg: int, seed: Optional[int] = None, with_tensors: bool = True) -> Wor
     if cfg == 4:
         return make_partitions(name, s, N=75600, H=40, d=128, with_tensors=with_tensors)
     if cfg == 5:
+        if chunk_select is None:
+            raise ValueError("workload 5 selects its chunks from Q and K: pass chunk_select")
         return make_chunk_gqa(name, s, B=4, Hq=64, Hkv=8, d=128, Nk=262144, Nq=2048, chunk=64, topk=2048,
-                              with_tensors=with_tensors)
+                              chunk_select=chunk_select, with_tensors=with_tensors)
     raise ValueError(f"unknown config {cfg}")
 
 
