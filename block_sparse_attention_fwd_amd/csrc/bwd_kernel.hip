@@ -11,7 +11,7 @@
 // Ownership, no atomics: a dK/dV workgroup owns 64 key slots of one K block (the K/V side
 // of a page never straddles blocks) and walks the transposed page list of that block -- the
 // 16-row Q pages of every Q block that selects it, packed two per 32-query stage across Q
-// block boundaries as they are loaded into LDS.  A dQ workgroup owns 64 query slots of one
+// block boundaries as they are loaded into LDS.  A dQ workgroup owns 128 query slots of one
 // Q block and walks the forward's K page list of that block, two pages per 32-key stage.
 // Each wave works on 32 owned rows; the owned operands stay in registers and the streamed
 // side comes through LDS.  Every product is v_mfma_f32_32x32x16_bf16 with fp32
@@ -140,6 +140,16 @@ struct PageRows {
                                                (int)(tok[n] * sn_b + cb[n]), 0, 0, 0);
     }
   }
+  // the page's rows of one tensor, straight into rows 16 page .. 16 page + 15 of dst
+  __device__ __forceinline__ void fire1(const uint32_t (&tok)[C::kInst], const __amdgpu_buffer_rsrc_t& r,
+                                        uint32_t sn, uint8_t* dst, int page) const {
+#pragma unroll
+    for (int n = 0; n < C::kInst; ++n) {
+      const int row = 16 * page + n * C::kRowsPerInst;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS_AS void*)(dst + row * C::kRowBytes), 16,
+                                               (int)(tok[n] * sn + cb[n]), 0, 0, 0);
+    }
+  }
   __device__ __forceinline__ void store(const u32x4 (&reg)[C::kInst], uint8_t* buf, int wave, int lane) const {
 #pragma unroll
     for (int n = 0; n < C::kInst; ++n)
@@ -192,9 +202,12 @@ __device__ __forceinline__ void store_rows(__bf16* dst, const f32x16 (&acc)[BwdC
 }
 
 // ---------------------------------------------------------------------------------------
-// dQ: one workgroup (2 waves) per (batch, head, 64-row Q tile).
+// dQ: one workgroup (4 waves, 32 query rows each) per (batch, head, 128-row Q tile).  The
+// four waves share every K/V stage: waves 0 and 1 load its two K pages, waves 2 and 3 its two
+// V pages.  A wave whose 32 rows are all past the tile's valid rows keeps its loads and
+// barriers and skips the products.
 template <int D, bool KPERM>
-__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dq_kernel(BwdParams p) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dq_kernel(BwdParams p) {
   using C = BwdCfg<D>;
   // the two stage buffers of K and of V as four objects, so that the compiler can tell the
   // loads into one buffer from the reads of the other and waits only for the stage it reads
@@ -222,6 +235,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))
   // this lane's query: Q^T and dO^T B operands, its LSE (log2 units) and D
   const int qrow = wave * 32 + (lane & 31);
   const bool qvalid = qrow < rows;
+  const bool active = wave * 32 < rows;  // the wave holds a valid row (uniform)
   const int qslot = row0 + (qvalid ? qrow : 0);
   const int qtok = p.qperm ? p.qperm[qslot] : qslot;
   bf16x8 qreg[C::kDS], goreg[C::kDS];
@@ -253,16 +267,19 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))
   uint32_t tok[C::kInst];  // tokens of the next stage to fire
   int gst = 0;             // stage of the next gather
   auto gather = [&]() {
-    const int e = e0 + 2 * gst + wave;  // entries past the list read as empty pages
+    const int e = e0 + 2 * gst + (wave & 1);  // entries past the list read as empty pages
     pr.template gather<KPERM>(e < e1 ? pl_ent[e] : 0, p.kperm, tok);
     ++gst;
   };
   auto fire = [&](uint8_t* kdst, uint8_t* vdst) __attribute__((always_inline)) {
-    pr.fire(tok, krsrc, p.k_sn_bytes, kdst, vrsrc, p.v_sn_bytes, vdst, wave);
+    if (wave < 2)
+      pr.fire1(tok, krsrc, p.k_sn_bytes, kdst, wave & 1);
+    else
+      pr.fire1(tok, vrsrc, p.v_sn_bytes, vdst, wave & 1);
   };
-  // VMEM loads issued after a stage's pages by the time its wait runs: the next stage's
-  // pages and, with a permutation, the gather of the stage after
-  constexpr int kAfter = 2 * C::kInst + (KPERM ? C::kInst : 0);
+  // VMEM loads issued after a stage's page by the time its wait runs: the next stage's
+  // page and, with a permutation, the gather of the stage after
+  constexpr int kAfter = C::kInst + (KPERM ? C::kInst : 0);
 
   f32x16 dqacc[C::kDB];
 #pragma unroll
@@ -283,6 +300,7 @@ __global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))
       wait_vmcnt<0>();
     }
     lds_barrier();
+    if (!active) return;
 
     f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
@@ -675,9 +693,9 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
   const int64_t n_dq = (int64_t)p.B * p.Hq * p.n_dq_tiles;
   if (n_dq > 0) {
     if (p.kperm)
-      hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)n_dq), dim3(128), 0, stream, p);
+      hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)n_dq), dim3(256), 0, stream, p);
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)n_dq), dim3(128), 0, stream, p);
+      hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)n_dq), dim3(256), 0, stream, p);
   }
   return hipGetLastError();
 }

@@ -62,7 +62,7 @@ struct BwdParams {
   int64_t k_sb, k_sn, k_sh;
   int64_t v_sb, v_sn, v_sh;
   int64_t o_sb, o_sn, o_sh;
-  const QTileDev* dq_tiles;   // 64-row Q tiles (row0, rows, qblock)
+  const QTileDev* dq_tiles;   // 128-row Q tiles (row0, rows, qblock)
   const QTileDev* kv_tiles;   // 64-row K tiles (first slot, rows, kblock)
   const int32_t* pl_ptr;      // K pages per (unit, Q block), as in the forward
   const int32_t* pl_ent;

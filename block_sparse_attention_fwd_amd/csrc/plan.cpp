@@ -242,7 +242,8 @@ int build_plan(const bsattn_problem& prob, const bsattn_layout& ql, const bsattn
   p->stats.n_units = n_units;
 
   // backward tables.  Q pages: a Q block of n slots has ceil(n/16) pages, like the K side.
-  // 64-row tiles of each side (a block of n slots gives ceil(n/64) tiles, the last one short).
+  // Owned tiles of each side: 128-row dQ tiles of each Q block, 64-row dK/dV tiles of each K
+  // block (a block of n slots gives ceil(n/rows) tiles, the last one short).
   // Transposed lists: for each (unit, K block), the Q pages of every Q block that selects
   // it -- Q blocks ascending, pages ascending -- so the K/V tile that owns a key walks
   // exactly the queries in the graph with it (KPage abstract, sentence 4: K/V-owned pages in
@@ -256,14 +257,14 @@ int build_plan(const bsattn_problem& prob, const bsattn_layout& ql, const bsattn
       p->qpage_nvalid.push_back(std::min(kPage, n - pg * kPage));
     }
     first_qpage[qb + 1] = int32_t(p->qpage_qblock.size());
-    for (int32_t r = 0; r < n; r += kBwdTileRows) {
-      p->dqt_qblock.push_back(qb); p->dqt_row0.push_back(s0 + r); p->dqt_rows.push_back(std::min(kBwdTileRows, n - r));
+    for (int32_t r = 0; r < n; r += kDqTileRows) {
+      p->dqt_qblock.push_back(qb); p->dqt_row0.push_back(s0 + r); p->dqt_rows.push_back(std::min(kDqTileRows, n - r));
     }
   }
   for (int32_t kb = 0; kb < nkb; ++kb) {
     const int32_t s0 = kl.offsets[kb], n = kl.offsets[kb + 1] - s0;
-    for (int32_t r = 0; r < n; r += kBwdTileRows) {
-      p->kvt_kblock.push_back(kb); p->kvt_row0.push_back(s0 + r); p->kvt_rows.push_back(std::min(kBwdTileRows, n - r));
+    for (int32_t r = 0; r < n; r += kKvTileRows) {
+      p->kvt_kblock.push_back(kb); p->kvt_row0.push_back(s0 + r); p->kvt_rows.push_back(std::min(kKvTileRows, n - r));
     }
   }
   {

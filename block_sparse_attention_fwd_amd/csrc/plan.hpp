@@ -31,7 +31,8 @@ constexpr int kStagePages = 4;
 constexpr size_t kEntryPad = 64;
 constexpr size_t kPermPad = 16;
 // backward tiles: 64 rows of one block on either side (two waves of 32 rows)
-constexpr int kBwdTileRows = 64;
+constexpr int kDqTileRows = 128;  // rows of a dQ tile (one Q block's slots)
+constexpr int kKvTileRows = 64;   // rows of a dK/dV tile (one K block's slots)
 
 }  // namespace bsattn
 

@@ -130,8 +130,9 @@ typedef struct bsattn_plan_view {
 
 /* Backward tables of a plan (views into plan memory, valid until bsattn_plan_destroy).
  * Q pages: each Q block of n slots has ceil(n/16) pages of 16 valid rows (the last may be
- * short), ordered by Q block then page.  Tiles of 64 slots of one block on each side
- * (ceil(n/64) per block, the last one short), ordered by block then row.  tpl_ptr/tpl_pages
+ * short), ordered by Q block then page.  Owned tiles of one block on each side, ordered
+ * by block then row: 128 slots per dQ tile of a Q block and 64 per dK/dV tile of a K block
+ * (ceil(n/height) per block, the last one short).  tpl_ptr/tpl_pages
  * give, for each (unit, K block) row = unit * n_kblocks + kblock, the Q page ids of every Q
  * block whose selection holds that K block: Q blocks ascending, each block's pages
  * ascending (KPage abstract, sentence 4: the K/V side owns its rows in backward). */
@@ -143,7 +144,7 @@ typedef struct bsattn_plan_bwd_view {
   int64_t n_dq_tiles;
   const int32_t* dqt_qblock;
   const int32_t* dqt_row0;     /* first slot in the Q layout */
-  const int32_t* dqt_rows;     /* 1..64 */
+  const int32_t* dqt_rows;     /* 1..128 */
   int64_t n_kv_tiles;
   const int32_t* kvt_kblock;
   const int32_t* kvt_row0;     /* first slot in the K layout */

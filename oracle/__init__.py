@@ -13,7 +13,7 @@ Contents
   planner.py    the page / tile plan: 16-row K/V pages owned by one block, Q-block
                 routing between 128x128 and 64x256 tiles, per-(unit, Q block) page
                 lists and the useful / physical query-key pair counts; the backward
-                tables (Q pages, 64-slot tiles of each side, Q page lists per
+                tables (Q pages, owned tiles of each side, Q page lists per
                 (unit, K block)).
   chunk_index.py  chunk selection: mean-key chunk summaries, one indexing query per
                 KV group, top-k chunks (CISA abstract, sentences 3-5).

@@ -209,13 +209,16 @@ def build_plan_w(w, fixed_tiles=False) -> Plan:
 # backward tables
 # ----------------------------------------------------------------------------
 # KPage abstract, sentence 4: the backward also walks pages that each belong to one
-# K/V block, on the selected pairs only.  Readings: the key side owns its rows -- each K block is cut into 64-slot tiles
-# (ceil(n/64) per block, the last one short) -- and the query side is streamed in 16-row Q
-# pages (a Q block of n slots has ceil(n/16) pages, as the K side in R2).  For each
-# (unit, K block) the Q pages to visit are those of every Q block whose selection row holds
-# that K block, Q blocks ascending and each block's pages ascending.  The dQ side owns
-# 64-slot tiles of each Q block and reuses the forward's page lists (R5).
-BWD_TILE = 64
+# K/V block, on the selected pairs only.  Readings: the key side owns its rows -- each K
+# block is cut into tiles of BWD_KV_TILE slots (ceil(n/BWD_KV_TILE) per block, the last one
+# short) -- and the query side is streamed in 16-row Q pages (a Q block of n slots has
+# ceil(n/16) pages, as the K side in R2).  For each (unit, K block) the Q pages to visit are
+# those of every Q block whose selection row holds that K block, Q blocks ascending and each
+# block's pages ascending.  The dQ side owns tiles of BWD_DQ_TILE slots of each Q block and
+# reuses the forward's page lists (R5).  The tile heights are a work split the page leaves
+# open (it fixes only that each key row has one owner); these are the kernels' heights.
+BWD_DQ_TILE = 128
+BWD_KV_TILE = 64
 
 
 @dataclasses.dataclass
@@ -247,18 +250,18 @@ def build_bwd_plan(q_offsets, k_offsets, sel_nb, sel_nh, sel_row_ptr, sel_kblk) 
             qpn.append(min(PAGE, n - p0))
         pages_of_qblock.append(ids)
 
-    def tiles(offsets):
+    def tiles(offsets, height):
         blk, row0, rows = [], [], []
         for b in range(len(offsets) - 1):
             s0, n = int(offsets[b]), int(offsets[b + 1] - offsets[b])
-            for r in range(0, n, BWD_TILE):
+            for r in range(0, n, height):
                 blk.append(b)
                 row0.append(s0 + r)
-                rows.append(min(BWD_TILE, n - r))
+                rows.append(min(height, n - r))
         return blk, row0, rows
 
-    dq = tiles(q_offsets)
-    kv = tiles(k_offsets)
+    dq = tiles(q_offsets, BWD_DQ_TILE)
+    kv = tiles(k_offsets, BWD_KV_TILE)
     n_units = sel_nb * sel_nh
     ptr = [0]
     pages = []

@@ -239,8 +239,8 @@ def test_cube_physical_independent_derivation():
 def test_bwd_lists_enumerate_graph_transpose(seed):
     """Brute force over (unit, query slot, key block): the Q page list of (unit, K block)
     covers exactly the query slots whose Q block selects that K block, each once, in slot
-    order; its pages never straddle Q blocks; the 64-slot tiles of each side partition
-    every block in order."""
+    order; its pages never straddle Q blocks; the owned tiles of each side (128 slots on the
+    Q side, 64 on the K side) partition every block in order."""
     from oracle.planner import build_bwd_plan_w
     w = make_random(seed, B=2, Hq=4, Hkv=2, Nq=300, Nk=260, d=64, max_qblock=70, max_kblock=50, density=0.35,
                     sel_mode="batch-kv", allow_empty=True, unsorted=True, dup=True, with_tensors=False)
@@ -261,11 +261,13 @@ def test_bwd_lists_enumerate_graph_transpose(seed):
                     if kb in set(w.sel_kblk[w.sel_row_ptr[u * nqb + qblk_of_slot[s]]:
                                             w.sel_row_ptr[u * nqb + qblk_of_slot[s] + 1]].tolist())]
             assert slots == want, (u, kb)
-    for offs, blk, row0, rows in ((w.q_offsets, bp.dqt_qblock, bp.dqt_row0, bp.dqt_rows),
-                                  (w.k_offsets, bp.kvt_kblock, bp.kvt_row0, bp.kvt_rows)):
+    for offs, blk, row0, rows, height in ((w.q_offsets, bp.dqt_qblock, bp.dqt_row0, bp.dqt_rows, 128),
+                                          (w.k_offsets, bp.kvt_kblock, bp.kvt_row0, bp.kvt_rows, 64)):
         covered = []
         for b, r0, n in zip(blk, row0, rows):
-            assert 1 <= n <= 64 and offs[b] <= r0 and r0 + n <= offs[b + 1]
+            assert 1 <= n <= height and offs[b] <= r0 and r0 + n <= offs[b + 1]
+            # a block's tiles are full except its last
+            assert n == height or r0 + n == offs[b + 1]
             covered.extend(range(r0, r0 + n))
         assert covered == list(range(int(offs[-1])))
 
