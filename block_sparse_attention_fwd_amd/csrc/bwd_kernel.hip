@@ -391,7 +391,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 // Waves 2 and 3 (gradient waves) hold the dK^T and dV^T accumulators of the same keys and
 // apply those operands one stage later.  Splitting the roles keeps every wave under 256
 // VGPRs, so two workgroups share a CU (two waves per SIMD) and each wave's phase hides the
-// other's latencies; the MFMA count per stage is the same as with one wave doing both.
+// other's latencies; the MFMA count per stage is the same as with one wave doing both.  The
+// score and gradient waves of a key half with no valid key keep their loads and barriers
+// and skip the products.
 // Pipeline: score waves load the Q pages (and the row statistics), gradient waves the dO
 // pages, through registers, two stages ahead; Q and dO have three stage buffers (the score
 // waves read stage it while the gradient waves read stage it - 1 and stage it + 1 is
@@ -422,6 +424,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   // this lane's key
   const int krow = kh * 32 + (lane & 31);
   const bool kvalid = krow < rows;
+  const bool active = kh * 32 < rows;  // the half holds a valid key (uniform)
   const int kslot = slot0 + (kvalid ? krow : 0);
   const int ktok = p.kperm ? p.kperm[kslot] : kslot;
 
@@ -577,7 +580,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         load();                            // stage it + 2
         gather();                          // tokens of stage it + 3
       }
-      if (it < nst) {
+      if (it < nst && active) {
         const uint8_t* qb = sq + B * C::kStage;
         const uint8_t* gb = sg + B * C::kStage;
         f32x16 sacc = f32x16{}, dpacc = f32x16{};
@@ -646,7 +649,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       load();
       gather();
     }
-    if (it >= 1) {  // stage it - 1
+    if (it >= 1 && active) {  // stage it - 1
       const int pb_ = cur == 0 ? 2 : cur - 1;
       const uint8_t* qb = sq + pb_ * C::kStage;
       const uint8_t* gb = sg + pb_ * C::kStage;
