@@ -382,6 +382,8 @@ def main():
                     help="time the chunk selection instead (default workload then 5: chunk-indexed GQA prefill)")
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward pass instead (default workload then 4: independent Q/K partitions)")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="only run the dense-MFMA calibration (random and zero operands) and print its rates")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB, 5 times (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -403,6 +405,16 @@ def main():
             c.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
+        return
+
+    if args.mfma_probe:
+        torch.cuda.set_device(0)
+        res = {}
+        for random in (True, False):
+            tf, ghz, ms = bs.mfma_probe(iters=400000, random=random)
+            res["random" if random else "zero"] = {"tflops": round(tf, 1), "ghz": round(ghz, 3), "ms": round(ms, 2)}
+        print(json.dumps({"mfma_probe": res, "mfma": "v_mfma_f32_32x32x16_bf16",
+                          "peak_tflops": PEAK_BF16_TFLOPS}), flush=True)
         return
 
     if args.workload is None:
@@ -504,6 +516,15 @@ def main():
                 "lds_bank_conflict_cycles": int(kv[f"{tag}.lds_bank_conflict_cycles"])
                 if f"{tag}.lds_bank_conflict_cycles" in kv else None,
                 "l2_hit_pct": float(kv[f"{tag}.l2_hit_pct"]) if f"{tag}.l2_hit_pct" in kv else None}
+
+    # the rate the matrix cores sustain on this product alone, under the same power limit
+    # (register operands of unit-normal-like spread, every SIMD busy; about half a second)
+    probe_tf, probe_ghz, _ = bs.mfma_probe(iters=200000, random=True)
+    roofline["mfma_probe_tflops"] = round(probe_tf, 1)
+    roofline["mfma_probe_ghz"] = round(probe_ghz, 3)
+    roofline["frac_of_mfma_probe"] = round(achieved / probe_tf, 4)
+    log(f"[bench] dense-MFMA probe: {probe_tf:.1f} TFLOP/s at {probe_ghz:.3f} GHz; the launch reaches "
+        f"{achieved / probe_tf:.3f} of it")
 
     cpu = None
     if args.cpu_seconds > 0:

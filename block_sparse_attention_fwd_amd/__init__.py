@@ -96,7 +96,7 @@ EXPORTED = ["bsattn_plan_create", "bsattn_plan_create_ex", "bsattn_plan_set_bloc
             "bsattn_plan_export", "bsattn_plan_export_bwd", "bsattn_fwd", "bsattn_fwd_shape",
             "bsattn_bwd_workspace_bytes", "bsattn_bwd", "bsattn_chunk_select", "bsattn_decode_workspace_bytes",
             "bsattn_fwd_decode", "bsattn_fwd_decode_noalloc", "bsattn_plan_update_selection", "bsattn_plan_destroy",
-            "bsattn_status_string",
+            "bsattn_mfma_probe", "bsattn_status_string",
             "bsattn_last_hip_error"]
 
 
@@ -129,6 +129,7 @@ def library() -> ctypes.CDLL:
     lib.bsattn_fwd_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp]
     lib.bsattn_plan_update_selection.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp]
     lib.bsattn_chunk_select.argtypes = [ctypes.POINTER(ChunkProblem), vp, vp, vp, vp, vp]
+    lib.bsattn_mfma_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp]
     lib.bsattn_plan_destroy.argtypes = [vp]
     lib.bsattn_status_string.argtypes = [ctypes.c_int]
     lib.bsattn_status_string.restype = ctypes.c_char_p
@@ -294,6 +295,33 @@ def bsattn_chunk_select(problem: ChunkProblem, q_ptr: int, k_ptr: int, summ_ptr:
     vp = ctypes.c_void_p
     _check(library().bsattn_chunk_select(ctypes.byref(problem), vp(q_ptr), vp(k_ptr), vp(summ_ptr), vp(chunks_ptr),
                                          vp(stream)), "bsattn_chunk_select")
+
+
+def bsattn_mfma_probe(n_workgroups: int, iters: int, random: bool, clocks_ptr: int, stream: int = 0) -> None:
+    vp = ctypes.c_void_p
+    _check(library().bsattn_mfma_probe(n_workgroups, iters, 1 if random else 0, vp(clocks_ptr), vp(stream)),
+           "bsattn_mfma_probe")
+
+
+def mfma_probe(iters: int = 200000, random: bool = True, n_workgroups: int = 512, repeats: int = 2):
+    """Sustained rate of the forward's MFMA on register operands alone (bsattn_mfma_probe):
+    ``repeats`` launches back to back, the last one timed with HIP events on the current
+    stream.  Returns (TFLOP/s, mean shader clock in GHz, launch ms)."""
+    import torch
+    clocks = torch.zeros(2 * n_workgroups, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for r in range(repeats):
+        if r == repeats - 1:
+            e0.record(stream)
+        bsattn_mfma_probe(n_workgroups, iters, random, clocks.data_ptr(), stream.cuda_stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    c = clocks.view(-1, 2).cpu().double()
+    ghz = float(c[:, 0].sum() / (c[:, 1].sum() / 100e6)) / 1e9
+    flop = float(n_workgroups) * 4 * iters * 32 * 32768.0
+    return flop / (ms * 1e-3) / 1e12, ghz, ms
 
 
 def chunk_select(q, k, Hkv: int, chunk: int, topk: int, query_index: int = -1, stream=None):

@@ -17,6 +17,7 @@ hipError_t launch_bwd(const BwdParams& p, int d, hipStream_t stream);
 hipError_t launch_chunk_select(const ChunkParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t stream);
 hipError_t launch_plan_update(const PlanUpdateParams& p, hipStream_t stream);
+hipError_t launch_mfma_probe(int n_workgroups, int iters, int random, uint64_t* clocks, hipStream_t stream);
 hipError_t decode_scratch(void** ptr, size_t* bytes);
 }
 
@@ -462,6 +463,14 @@ int bsattn_chunk_select(const bsattn_chunk_problem* pr, const void* q, const voi
   while (np2 < n) np2 <<= 1;
   cp.n_pad = np2;
   hipError_t e = bsattn::launch_chunk_select(cp, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return BSATTN_OK;
+}
+
+int bsattn_mfma_probe(int32_t n_workgroups, int32_t iters, int32_t random, uint64_t* clocks, void* stream) {
+  if (clocks == nullptr || iters < 1 || n_workgroups < 1 || n_workgroups > 65535) return BSATTN_E_ARG;
+  if ((reinterpret_cast<uintptr_t>(clocks) & 7) != 0) return BSATTN_E_ARG;
+  hipError_t e = bsattn::launch_mfma_probe(n_workgroups, iters, random != 0, clocks, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e);
   return BSATTN_OK;
 }

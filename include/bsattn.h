@@ -332,6 +332,22 @@ typedef struct bsattn_chunk_problem {
 int bsattn_chunk_select(const bsattn_chunk_problem* problem, const void* q, const void* k, float* summaries,
                         int32_t* chunks, void* stream);
 
+/* Dense-MFMA calibration, a measurement aid beside the attention calls: the rate at which
+ * the matrix cores run the forward's product (v_mfma_f32_32x32x16_bf16, bf16 in, fp32
+ * accumulate) with nothing else on the chip, for quoting a kernel's rate against what the
+ * chip sustains under its power limit as well as against the nominal peak.  One kernel of
+ * n_workgroups workgroups of 4 waves (2 per CU fills every SIMD with two waves); each wave
+ * issues iters x 32 products on register operands (1,048,576 FLOPs per wave and iteration),
+ * pseudo-random bf16 of unit-normal-like spread when random != 0, zeros otherwise.  The
+ * first wave of workgroup i writes clocks[2 i] = shader-clock cycles and clocks[2 i + 1] =
+ * 100 MHz real-time ticks spent in its loop; the caller times the launch (FLOPs =
+ * n_workgroups x 4 x iters x 32 x 32768) and takes the mean shader clock as the sum of the
+ * cycle spans over the sum of the tick spans x 100 MHz.  clocks: caller-owned device
+ * memory of 16 x n_workgroups bytes, 8-byte aligned, written.  Asynchronous on stream; no
+ * allocation.  Errors: BSATTN_E_ARG (null or misaligned clocks, iters < 1, n_workgroups
+ * outside 1..65535), BSATTN_E_HIP on a launch error. */
+int bsattn_mfma_probe(int32_t n_workgroups, int32_t iters, int32_t random, uint64_t* clocks, void* stream);
+
 int bsattn_plan_destroy(bsattn_plan* plan);
 
 const char* bsattn_status_string(int status);

@@ -171,6 +171,17 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(bs.library(), name)
 
 
+def test_mfma_probe_argument_errors():
+    # rejected before anything touches the GPU: null or misaligned clock buffer, no
+    # iterations, a grid outside 1..65535 workgroups
+    lib = bs.library()
+    assert lib.bsattn_mfma_probe(512, 10, 1, None, None) == 1
+    assert lib.bsattn_mfma_probe(512, 10, 1, ctypes.c_void_p(12), None) == 1
+    assert lib.bsattn_mfma_probe(512, 0, 1, ctypes.c_void_p(256), None) == 1
+    assert lib.bsattn_mfma_probe(0, 10, 1, ctypes.c_void_p(256), None) == 1
+    assert lib.bsattn_mfma_probe(65536, 10, 1, ctypes.c_void_p(256), None) == 1
+
+
 def test_chunk_select_argument_errors():
     def st(**kw):
         pr = bs.ChunkProblem()
