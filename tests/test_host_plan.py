@@ -265,3 +265,25 @@ def test_update_selection_needs_upload():
     with pytest.raises(bs.BsattnError) as e:
         bs.bsattn_plan_update_selection(p.handle, w.sel_nb, w.sel_nh, 256, 256)
     assert e.value.status == 7
+
+
+# Property-based sweep of the same bit-exact comparison: hypothesis draws the problem shape,
+# the layouts (block sizes, empty blocks, permutations), the selection (density, sharing
+# mode, unsorted rows with duplicates), causality and the plan flags.
+from hypothesis import given, settings, HealthCheck, strategies as hst  # noqa: E402
+
+
+@settings(max_examples=150, deadline=None, suppress_health_check=[HealthCheck.too_slow], derandomize=True)
+@given(seed=hst.integers(0, 1 << 20), B=hst.integers(1, 2), Hkv=hst.sampled_from([1, 2]),
+       grp=hst.sampled_from([1, 2, 4]), Nq=hst.integers(1, 500), Nk=hst.integers(1, 500),
+       d=hst.sampled_from([64, 128]), max_qblock=hst.integers(1, 300), max_kblock=hst.integers(1, 140),
+       density=hst.floats(0.02, 1.0), sel_mode=hst.sampled_from(["shared", "kv", "head", "batch-kv"]),
+       allow_empty=hst.booleans(), use_perm=hst.booleans(), causal=hst.booleans(), unsorted=hst.booleans(),
+       dup=hst.booleans(), fixed=hst.booleans())
+def test_property_bit_exact(seed, B, Hkv, grp, Nq, Nk, d, max_qblock, max_kblock, density, sel_mode, allow_empty,
+                            use_perm, causal, unsorted, dup, fixed):
+    w = make_random(seed, B=B, Hq=Hkv * grp, Hkv=Hkv, Nq=Nq, Nk=Nk, d=d, max_qblock=max_qblock,
+                    max_kblock=max_kblock, density=density, sel_mode=sel_mode, allow_empty=allow_empty,
+                    use_perm=use_perm, causal=causal, unsorted=unsorted, dup=dup, with_tensors=False)
+    st = _compare(w, flags=bs.PLAN_FIXED_TILES if fixed else 0)
+    assert st["physical"] >= st["useful"] >= 0
