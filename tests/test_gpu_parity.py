@@ -234,3 +234,27 @@ def test_chunk_gqa_scaled_full():
 def test_chunk_gqa_full_size_sampled():
     w = make(5, chunk_select=oracle_chunk_select)
     check_sampled(w, "chunk-gqa", heads=[(0, 0), (1, 9), (3, 63)], n_rows=64, extra_rows=[0, 2047])
+
+
+# ---------------------------------------------------------------------------
+# fuzz: random shapes, layouts, selections and flags drawn from a seeded generator
+# ---------------------------------------------------------------------------
+def _fuzz_case(seed, base):
+    rng = np.random.default_rng(base + seed)
+    Hkv = int(rng.choice([1, 2]))
+    Hq = Hkv * int(rng.choice([1, 2, 4]))
+    causal = bool(rng.random() < 0.4)
+    kw = dict(B=int(rng.integers(1, 3)), Hq=Hq, Hkv=Hkv, Nq=int(rng.integers(1, 520)),
+              Nk=int(rng.integers(1, 520)), d=int(rng.choice([64, 128])), max_qblock=int(rng.integers(1, 260)),
+              max_kblock=int(rng.integers(1, 140)), density=float(rng.uniform(0.05, 0.9)),
+              sel_mode=str(rng.choice(["shared", "kv", "head", "batch-kv"])), allow_empty=bool(rng.random() < 0.4),
+              use_perm=bool(rng.random() < 0.4), causal=causal, unsorted=bool(rng.random() < 0.3),
+              dup=bool(rng.random() < 0.3))
+    if causal:
+        kw["q_pos0"] = int(rng.integers(-100, 200))
+    return make_random(base + 1000 + seed, **kw)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_fuzz_full(seed):
+    check_full(_fuzz_case(seed, 3000), f"fuzz-{seed}")
