@@ -388,8 +388,8 @@ def main():
                     help="only run a plain device copy of this many MiB, 5 times (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
-              "(the forward pass shards over (batch, head) with no exchange; see the design notes).",
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the forward pass would shard over (batch, head) with no exchange between GPUs).",
               file=sys.stderr)
         sys.exit(2)
 
