@@ -394,8 +394,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 // other's latencies; the MFMA count per stage is the same as with one wave doing both.  The
 // score and gradient waves of a key half with no valid key keep their loads and barriers
 // and skip the products.
-// Pipeline: score waves load the Q pages (and the row statistics), gradient waves the dO
-// pages, through registers, two stages ahead; Q and dO have three stage buffers (the score
+// Pipeline: score waves load the Q pages, gradient waves the dO pages and the row
+// statistics (LSE, D and the causal bound of each query row; the gradient waves have slack at
+// the barrier, the score waves set the pace), through registers, two stages ahead; Q and dO have three stage buffers (the score
 // waves read stage it while the gradient waves read stage it - 1 and stage it + 1 is
 // written), the operands two.  One barrier per iteration, the same count in both roles.
 template <int D, bool QPERM>
@@ -478,7 +479,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     n_h = f_h;
     n_ent = f_ok ? __builtin_amdgcn_readfirstlane((int)f_raw) : 0;
     pr.template gather<QPERM>(n_ent, p.qperm, tok);
-    if (score) {
+    if (!score) {
       const int r = lane & 15;
       const int slot = ent_slot(n_ent) + (r < ent_nv(n_ent) ? r : 0);
       n_stok = QPERM ? p.qperm[slot] : slot;
@@ -487,7 +488,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     fetch();  // the stage after
   };
   // the loaded page, not yet in LDS: Q (score waves) or dO (gradient waves) rows, and the
-  // row statistics (score waves)
+  // row statistics (gradient waves)
   u32x4 rr[C::kInst];
   float r_lse = 0.f, r_d = 0.f;
   int r_tok = 0, r_nv = 0;
@@ -504,29 +505,29 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       if (score) {
         const char* qslice = reinterpret_cast<const char*>(p.q) + ((int64_t)b * p.q_sb + (int64_t)h * p.q_sh) * 2;
         t_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)qslice, (short)0, p.q_extent, 0x00020000);
-        const int64_t srow = ((int64_t)b * p.Hq + h) * p.Nq;
-        lse_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(p.lse + srow), (short)0, (uint32_t)p.Nq * 4u, 0x00020000);
-        d_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(p.dvec + srow), (short)0, (uint32_t)p.Nq * 4u, 0x00020000);
       } else {
         const char* gslice = reinterpret_cast<const char*>(p.dout) + ((int64_t)b * p.o_sb + (int64_t)h * p.o_sh) * 2;
         t_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)gslice, (short)0, p.o_extent, 0x00020000);
+        const int64_t srow = ((int64_t)b * p.Hq + h) * p.Nq;
+        lse_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(p.lse + srow), (short)0, (uint32_t)p.Nq * 4u, 0x00020000);
+        d_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(p.dvec + srow), (short)0, (uint32_t)p.Nq * 4u, 0x00020000);
       }
     }
     if (score) {
       pr.load(tok, t_rsrc, p.q_sn_bytes, rr);
+    } else {
+      pr.load(tok, t_rsrc, p.o_sn_bytes, rr);
       r_lse = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lse_rsrc, n_stok * 4, 0, 0));
       r_d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(d_rsrc, n_stok * 4, 0, 0));
       r_tok = n_stok;
       r_nv = ent_nv(n_ent);
-    } else {
-      pr.load(tok, t_rsrc, p.o_sn_bytes, rr);
     }
   };
-  // page kh of stage buffer `buf`: rows 16 kh .. 16 kh + 15; lanes 0..15 of a score wave
-  // write the statistics of those rows
+  // page kh of stage buffer `buf`: rows 16 kh .. 16 kh + 15; lanes 0..15 of a gradient wave
+  // write the statistics of those rows (for the score waves of the next iteration)
   auto store = [&](int buf, int sbuf) {
     pr.store(rr, (score ? sq : sg) + buf * C::kStage, kh, lane);
-    if (score && lane < 16) {
+    if (!score && lane < 16) {
       const bool valid = lane < r_nv;
       s_lse[sbuf][16 * kh + lane] = (valid && r_lse != kNegInf) ? r_lse * kLog2e : __builtin_huge_valf();
       s_d[sbuf][16 * kh + lane] = valid ? r_d : 0.f;
@@ -645,7 +646,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int it = 0; it < n_it; ++it) {
     lds_barrier();  // matches the score waves' barrier of the same iteration
     if (it + 1 < nst) {
-      store(cur == 2 ? 0 : cur + 1, 0);
+      store(cur == 2 ? 0 : cur + 1, (it + 1) & 1);
       load();
       gather();
     }
