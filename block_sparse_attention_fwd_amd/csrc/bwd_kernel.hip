@@ -395,10 +395,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 // score and gradient waves of a key half with no valid key keep their loads and barriers
 // and skip the products.
 // Pipeline: score waves load the Q pages, gradient waves the dO pages and the row
-// statistics (LSE, D and the causal bound of each query row; the gradient waves have slack at
-// the barrier, the score waves set the pace), through registers, two stages ahead; Q and dO have three stage buffers (the score
-// waves read stage it while the gradient waves read stage it - 1 and stage it + 1 is
-// written), the operands two.  One barrier per iteration, the same count in both roles.
+// statistics (LSE, D and the causal bound of each query row: the score waves set the pace,
+// the gradient waves have slack at the barrier), through registers, two stages ahead.  Q
+// and dO have three stage buffers (the score waves read stage it while the gradient waves
+// read stage it - 1 and stage it + 1 is written), the operands two.  One barrier per
+// iteration, the same count in both roles.
 template <int D, bool QPERM>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dkdv_kernel(BwdParams p) {
   using C = BwdCfg<D>;
