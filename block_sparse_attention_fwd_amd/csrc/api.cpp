@@ -305,6 +305,7 @@ int run_bwd(const bsattn_plan* plan, const void* q, const void* k, const void* v
   bp.q_sn_bytes = uint32_t(pr.q_stride[1] * 2); bp.o_sn_bytes = uint32_t(pr.o_stride[1] * 2);
   bp.k_sn_bytes = uint32_t(pr.k_stride[1] * 2); bp.v_sn_bytes = uint32_t(pr.v_stride[1] * 2);
   bp.n_dq_tiles = int32_t(plan->dqt_row0.size());
+  bp.n_dq_split = plan->n_dqt_split;
   bp.n_kv_tiles = int32_t(plan->kvt_row0.size());
   bp.B = pr.B; bp.Hq = pr.Hq; bp.Hkv = pr.Hkv; bp.Nq = pr.Nq; bp.Nk = pr.Nk;
   bp.grp = pr.Hq / pr.Hkv;

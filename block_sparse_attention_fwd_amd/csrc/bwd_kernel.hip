@@ -206,15 +206,30 @@ __device__ __forceinline__ void store_rows(__bf16* dst, const f32x16 (&acc)[BwdC
 // four waves share every K/V stage: waves 0 and 1 load its two K pages, waves 2 and 3 its two
 // V pages.  A wave whose 32 rows are all past the tile's valid rows keeps its loads and
 // barriers and skips the products.
-template <int D, bool KPERM>
+// A tile of at most 64 valid rows splits its keys instead: waves w and w + 2 hold the same 32
+// rows (row group w & 1), wave w walks the even 32-key stages and wave w + 2 the odd ones,
+// each into its own pair of stage buffers, and the two partial sums of dQ are added through
+// LDS at the end.  Every wave then loads both the K and the V page of one page slot of its
+// stage, so a tile of 33..64 rows keeps all four waves busy on half as many iterations.
+// The two kinds of tile run as two launches (SPLIT): one kernel holding both walks needs
+// more than 256 VGPRs.  The plan's device image lists the short tiles last.
+template <int D, bool KPERM, bool SPLIT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_dq_kernel(BwdParams p) {
   using C = BwdCfg<D>;
-  // the two stage buffers of K and of V as four objects, so that the compiler can tell the
-  // loads into one buffer from the reads of the other and waits only for the stage it reads
+  // stage buffers as separate objects, so that the compiler can tell the loads into one
+  // buffer from the reads of another and waits only for the stage it reads: K and V of the
+  // two stages in flight (sk0/sv0, sk1/sv1), and for split tiles the odd stages' pair
+  // (sk2/sv2, sk3/sv3), which also holds the partial sums of the final merge
+  constexpr int kOdd = SPLIT ? C::kStage : 16;
   __shared__ __attribute__((aligned(1024))) uint8_t sk0[C::kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t sk1[C::kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t sv0[C::kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t sv1[C::kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t sk2[kOdd];
+  __shared__ __attribute__((aligned(1024))) uint8_t sk3[kOdd];
+  __shared__ __attribute__((aligned(1024))) uint8_t sv2[kOdd];
+  __shared__ __attribute__((aligned(1024))) uint8_t sv3[kOdd];
+  static_assert(C::kDB * 16 * 64 * 4 == 2 * C::kStage, "a wave's dQ accumulators fill two stage buffers");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hh = lane >> 5;
@@ -222,20 +237,24 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const CONST_AS int32_t* pl_ptr = (const CONST_AS int32_t*)p.pl_ptr;
   const CONST_AS int32_t* tiles = (const CONST_AS int32_t*)p.dq_tiles;
 
-  const int work = xcd_work(blockIdx.x, p.B * p.Hq * p.n_dq_tiles);
-  const int bh = work / p.n_dq_tiles;
-  const int t = work - bh * p.n_dq_tiles;
+  // this launch's tiles: the long ones first in the list, the short ones after them
+  const int n_tiles = SPLIT ? p.n_dq_split : p.n_dq_tiles - p.n_dq_split;
+  const int work = xcd_work(blockIdx.x, p.B * p.Hq * n_tiles);
+  const int bh = work / n_tiles;
+  const int t = work - bh * n_tiles + (SPLIT ? p.n_dq_tiles - p.n_dq_split : 0);
   const int b = bh / p.Hq, h = bh - b * p.Hq, g = h / p.grp;
   const int row0 = tiles[4 * t], rows = tiles[4 * t + 1], qblock = tiles[4 * t + 2];
   const int unit = (b * p.ub_mul) * p.sel_nh + h / p.uh_div;
   const int lrow = unit * p.nqb + qblock;
   const int e0 = pl_ptr[lrow], e1 = pl_ptr[lrow + 1];
   const int ns = (e1 - e0 + 1) >> 1;  // 32-key stages
+  const int rg = SPLIT ? (wave & 1) : wave;  // row group
+  const int kp = SPLIT ? (wave >> 1) : 0;    // split walk: even (0) or odd (1) stages
 
   // this lane's query: Q^T and dO^T B operands, its LSE (log2 units) and D
-  const int qrow = wave * 32 + (lane & 31);
+  const int qrow = rg * 32 + (lane & 31);
   const bool qvalid = qrow < rows;
-  const bool active = wave * 32 < rows;  // the wave holds a valid row (uniform)
+  const bool active = rg * 32 < rows;  // the wave holds a valid row (uniform)
   const int qslot = row0 + (qvalid ? qrow : 0);
   const int qtok = p.qperm ? p.qperm[qslot] : qslot;
   bf16x8 qreg[C::kDS], goreg[C::kDS];
@@ -286,22 +305,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int db = 0; db < C::kDB; ++db) dqacc[db] = f32x16{};
   const float sl2 = p.scale_log2;
 
-  // stage st: its K and V pages are in kb / vb; the next stage's go to kn / vn
-  // (NEXT: a stage follows; known at compile time, so the steady state has no branch)
-  auto stage = [&](auto next_tag, int st, const uint8_t* kb, const uint8_t* vb, uint8_t* kn, uint8_t* vn)
-                   __attribute__((always_inline)) {
-    if constexpr (decltype(next_tag)::value) {
-      lds_barrier();  // both waves are done with the other buffer (stage st - 1)
-      fire(kn, vn);   // stage st + 1
-      gather();       // tokens of stage st + 2
-      __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt<kAfter>();  // stage st landed
-    } else {
-      wait_vmcnt<0>();
-    }
-    lds_barrier();
-    if (!active) return;
-
+  // products of stage st (K and V pages in kb / vb) into dqacc
+  auto compute = [&](int st, const uint8_t* kb, const uint8_t* vb) __attribute__((always_inline)) {
     f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
     for (int s = 0; s < C::kDS; ++s) {
@@ -357,28 +362,129 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
       for (int db = 0; db < C::kDB; ++db)
         dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(kb, lane, half, db), dsb[half], dqacc[db], 0, 0, 0);
+  };
+
+  // stage st: its K and V pages are in kb / vb; the next stage's go to kn / vn
+  // (NEXT: a stage follows; known at compile time, so the steady state has no branch)
+  auto stage = [&](auto next_tag, int st, const uint8_t* kb, const uint8_t* vb, uint8_t* kn, uint8_t* vn)
+                   __attribute__((always_inline)) {
+    if constexpr (decltype(next_tag)::value) {
+      lds_barrier();  // both waves are done with the other buffer (stage st - 1)
+      fire(kn, vn);   // stage st + 1
+      gather();       // tokens of stage st + 2
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<kAfter>();  // stage st landed
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();
+    if (active) compute(st, kb, vb);
     // each stage is scheduled on its own: no work moves between the two buffers' copies
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  if (ns > 0) {
-    gather();
-    fire(sk0, sv0);
-    gather();
-  }
-  int st = 0;
-  for (; st + 2 < ns; st += 2) {
-    stage(BoolTag<true>{}, st, sk0, sv0, sk1, sv1);
-    stage(BoolTag<true>{}, st + 1, sk1, sv1, sk0, sv0);
-  }
-  if (st + 1 < ns) {
-    stage(BoolTag<true>{}, st, sk0, sv0, sk1, sv1);
-    stage(BoolTag<false>{}, st + 1, sk1, sv1, sk0, sv0);
-  } else if (st < ns) {
-    stage(BoolTag<false>{}, st, sk0, sv0, sk1, sv1);
+  // Split walk of a tile of at most 64 rows.  Iteration i covers stages 2i (KP = 0) and
+  // 2i + 1 (KP = 1); the KP waves read buffer pair (ka, va) on even i and (kb, vb) on odd i,
+  // and each wave loads page slot (wave & 1) of its stage of iteration i + 1, K and V, one
+  // iteration ahead.  KP is a template argument, so that every buffer is a fixed LDS object.
+  auto split_walk = [&](auto kp_tag) __attribute__((always_inline)) {
+    constexpr int KP = decltype(kp_tag)::value;
+    uint8_t* const ka = KP ? sk2 : sk0;
+    uint8_t* const va = KP ? sv2 : sv0;
+    uint8_t* const kb = KP ? sk3 : sk1;
+    uint8_t* const vb = KP ? sv3 : sv1;
+    const int npair = (ns + 1) >> 1;
+    int gi = 0;  // iteration of the next gather
+    auto sgather = [&]() {
+      const int e = e0 + 2 * (2 * gi + KP) + (wave & 1);  // entries past the list read as empty pages
+      pr.template gather<KPERM>(e < e1 ? pl_ent[e] : 0, p.kperm, tok);
+      ++gi;
+    };
+    // VMEM loads issued after an iteration's pages by the time its wait runs: the next
+    // iteration's K and V pages and, with a permutation, the gather of the one after
+    constexpr int kAfterSplit = 2 * C::kInst + (KPERM ? C::kInst : 0);
+    auto iter = [&](auto next_tag, int i, const uint8_t* kc, const uint8_t* vc, uint8_t* kn, uint8_t* vn)
+                    __attribute__((always_inline)) {
+      if constexpr (decltype(next_tag)::value) {
+        lds_barrier();  // every wave is done with the other buffer pair (iteration i - 1)
+        pr.fire1(tok, krsrc, p.k_sn_bytes, kn, wave & 1);  // iteration i + 1
+        pr.fire1(tok, vrsrc, p.v_sn_bytes, vn, wave & 1);
+        sgather();                                                                 // tokens of i + 2
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<kAfterSplit>();  // iteration i landed
+      } else {
+        wait_vmcnt<0>();
+      }
+      lds_barrier();
+      const int st = 2 * i + KP;
+      if (active && st < ns) compute(st, kc, vc);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (npair > 0) {
+      sgather();
+      pr.fire1(tok, krsrc, p.k_sn_bytes, ka, wave & 1);
+      pr.fire1(tok, vrsrc, p.v_sn_bytes, va, wave & 1);
+      sgather();
+    }
+    int i = 0;
+    for (; i + 2 < npair; i += 2) {
+      iter(BoolTag<true>{}, i, ka, va, kb, vb);
+      iter(BoolTag<true>{}, i + 1, kb, vb, ka, va);
+    }
+    if (i + 1 < npair) {
+      iter(BoolTag<true>{}, i, ka, va, kb, vb);
+      iter(BoolTag<false>{}, i + 1, kb, vb, ka, va);
+    } else if (i < npair) {
+      iter(BoolTag<false>{}, i, ka, va, kb, vb);
+    }
+  };
+
+  if constexpr (SPLIT) {
+    if (kp == 0)
+      split_walk(IntTag<0>{});
+    else
+      split_walk(IntTag<1>{});
+    // merge: the odd-stage waves hand their partial sums to the even-stage waves of the same
+    // rows through the odd buffers (row group 0 in sk2 / sk3, row group 1 in sv2 / sv3)
+    __syncthreads();
+    uint8_t* const r0 = rg ? sv2 : sk2;
+    uint8_t* const r1 = rg ? sv3 : sk3;
+    if (kp == 1 && active) {
+#pragma unroll
+      for (int db = 0; db < C::kDB; ++db) {
+        float* ob = reinterpret_cast<float*>((db < C::kDB / 2 ? r0 : r1)) + (db % (C::kDB / 2)) * 16 * 64;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ob[e * 64 + lane] = dqacc[db][e];
+      }
+    }
+    __syncthreads();
+    if (kp == 1 || !qvalid) return;
+#pragma unroll
+    for (int db = 0; db < C::kDB; ++db) {
+      const float* ob = reinterpret_cast<const float*>((db < C::kDB / 2 ? r0 : r1)) + (db % (C::kDB / 2)) * 16 * 64;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dqacc[db][e] += ob[e * 64 + lane];
+    }
+  } else {
+    if (ns > 0) {
+      gather();
+      fire(sk0, sv0);
+      gather();
+    }
+    int st = 0;
+    for (; st + 2 < ns; st += 2) {
+      stage(BoolTag<true>{}, st, sk0, sv0, sk1, sv1);
+      stage(BoolTag<true>{}, st + 1, sk1, sv1, sk0, sv0);
+    }
+    if (st + 1 < ns) {
+      stage(BoolTag<true>{}, st, sk0, sv0, sk1, sv1);
+      stage(BoolTag<false>{}, st + 1, sk1, sv1, sk0, sv0);
+    } else if (st < ns) {
+      stage(BoolTag<false>{}, st, sk0, sv0, sk1, sv1);
+    }
+    if (!qvalid) return;
   }
 
-  if (!qvalid) return;
   __bf16* dst = reinterpret_cast<__bf16*>(p.dq) + (int64_t)b * p.q_sb + (int64_t)qtok * p.q_sn + (int64_t)h * p.q_sh;
   store_rows<D>(dst, dqacc, p.scale, lane);
 }
@@ -695,12 +801,20 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t stream) {
     else
       hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3((unsigned)n_kv), dim3(256), 0, stream, p);
   }
-  const int64_t n_dq = (int64_t)p.B * p.Hq * p.n_dq_tiles;
-  if (n_dq > 0) {
+  // dQ: the tiles of more than kDqSplitRows rows, then the short tiles with the key split
+  const int64_t n_long = (int64_t)p.B * p.Hq * (p.n_dq_tiles - p.n_dq_split);
+  const int64_t n_short = (int64_t)p.B * p.Hq * p.n_dq_split;
+  if (n_long > 0) {
     if (p.kperm)
-      hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)n_dq), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((bwd_dq_kernel<D, true, false>), dim3((unsigned)n_long), dim3(256), 0, stream, p);
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)n_dq), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((bwd_dq_kernel<D, false, false>), dim3((unsigned)n_long), dim3(256), 0, stream, p);
+  }
+  if (n_short > 0) {
+    if (p.kperm)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, true, true>), dim3((unsigned)n_short), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<D, false, true>), dim3((unsigned)n_short), dim3(256), 0, stream, p);
   }
   return hipGetLastError();
 }

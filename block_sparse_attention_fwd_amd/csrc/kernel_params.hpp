@@ -6,6 +6,9 @@
 
 namespace bsattn {
 
+// dQ tiles of at most this many rows (two 32-row groups) split their keys over the waves
+constexpr int kDqSplitRows = 64;
+
 // XCDs (of the chip's 8) that work on one (batch, head) slice of the forward at a time.
 constexpr int kXcdShare = 1;
 
@@ -62,7 +65,9 @@ struct BwdParams {
   int64_t k_sb, k_sn, k_sh;
   int64_t v_sb, v_sn, v_sh;
   int64_t o_sb, o_sn, o_sh;
-  const QTileDev* dq_tiles;   // 128-row Q tiles (row0, rows, qblock)
+  const QTileDev* dq_tiles;   // 128-row Q tiles (row0, rows, qblock): the last n_dq_split
+                              // hold at most kDqSplitRows rows
+
   const QTileDev* kv_tiles;   // 64-row K tiles (first slot, rows, kblock)
   const int32_t* pl_ptr;      // K pages per (unit, Q block), as in the forward
   const int32_t* pl_ent;
@@ -73,7 +78,7 @@ struct BwdParams {
   int64_t q_pos0;
   uint32_t q_extent, o_extent, k_extent, v_extent;  // bytes of one (batch, head) slice
   uint32_t q_sn_bytes, o_sn_bytes, k_sn_bytes, v_sn_bytes;
-  int32_t n_dq_tiles, n_kv_tiles;
+  int32_t n_dq_tiles, n_kv_tiles, n_dq_split;
   int32_t B, Hq, Hkv, Nq, Nk, grp;
   int32_t nqb, nkb, sel_nh, ub_mul, uh_div;
   int32_t causal;

@@ -346,8 +346,18 @@ int build_plan(const bsattn_problem& prob, const bsattn_layout& ql, const bsattn
   }
   if (p->has_qperm) std::memcpy(img + p->off_qperm, ql.perm, sizeof(int32_t) * size_t(Nq));
   if (p->has_kperm) std::memcpy(img + p->off_kperm, kl.perm, sizeof(int32_t) * size_t(Nk));
+  // dQ tiles on the device: the tiles of more than kDqSplitRows rows first, then the short
+  // ones (each kind in plan order), which the backward runs in a launch of their own
   QTileDev* dqt = reinterpret_cast<QTileDev*>(img + p->off_dqt);
-  for (size_t t = 0; t < p->dqt_row0.size(); ++t) dqt[t] = QTileDev{p->dqt_row0[t], p->dqt_rows[t], p->dqt_qblock[t], 0};
+  {
+    size_t n = 0;
+    for (int pass = 0; pass < 2; ++pass)
+      for (size_t t = 0; t < p->dqt_row0.size(); ++t)
+        if ((p->dqt_rows[t] <= kDqSplitRows) == (pass == 1))
+          dqt[n++] = QTileDev{p->dqt_row0[t], p->dqt_rows[t], p->dqt_qblock[t], 0};
+    p->n_dqt_split = int32_t(std::count_if(p->dqt_rows.begin(), p->dqt_rows.end(),
+                                           [](int32_t r) { return r <= kDqSplitRows; }));
+  }
   QTileDev* kvt = reinterpret_cast<QTileDev*>(img + p->off_kvt);
   for (size_t t = 0; t < p->kvt_row0.size(); ++t) kvt[t] = QTileDev{p->kvt_row0[t], p->kvt_rows[t], p->kvt_kblock[t], 0};
   int32_t* fpg = reinterpret_cast<int32_t*>(img + p->off_firstpage);

@@ -51,6 +51,7 @@ struct bsattn_plan {
   std::vector<uint8_t> image;
   size_t off_qt[bsattn::kShapes] = {0, 0};
   int32_t n_qt[bsattn::kShapes] = {0, 0};
+  int32_t n_dqt_split = 0;  // dQ tiles of at most kDqSplitRows rows (last in the device image)
   size_t off_plptr = 0, off_plent = 0, off_qperm = 0, off_kperm = 0;
   bool has_qperm = false, has_kperm = false;
   // backward: Q pages (16 valid rows of one Q block), 64-row tiles of each side, and the

@@ -141,6 +141,13 @@ BWD_CASES = [
          density=1.0),
     dict(seed=208, B=1, Hq=2, Hkv=2, Nq=64, Nk=16, d=64, max_qblock=64, max_kblock=16, sel_mode="head",
          density=1.0),
+    # dQ tiles of both kinds (more than 64 rows, and 1..64 rows with the key split) with
+    # permuted keys under a causal mask at head dim 128
+    dict(seed=209, B=1, Hq=2, Hkv=1, Nq=620, Nk=580, d=128, max_qblock=90, max_kblock=45, sel_mode="kv",
+         causal=True, use_perm=True, allow_empty=True, density=0.35),
+    # only split dQ tiles (blocks of 1..64 rows), causal with identity layouts, head dim 64
+    dict(seed=210, B=1, Hq=2, Hkv=2, Nq=700, Nk=500, d=64, max_qblock=64, max_kblock=50, sel_mode="head",
+         causal=True, q_pos0=-40, density=0.4),
 ]
 
 
