@@ -12,7 +12,9 @@
 // of a page never straddles blocks) and walks the transposed page list of that block -- the
 // 16-row Q pages of every Q block that selects it, packed two per 32-query stage across Q
 // block boundaries as they are loaded into LDS.  A dQ workgroup owns 128 query slots of one
-// Q block and walks the forward's K page list of that block, two pages per 32-key stage.
+// Q block and walks the forward's K page list of that block, two pages per 32-key stage (a
+// tile of at most 64 rows gives its even and odd stages to two pairs of waves and adds the
+// two partial sums at the end).
 // Each wave works on 32 owned rows; the owned operands stay in registers and the streamed
 // side comes through LDS.  Every product is v_mfma_f32_32x32x16_bf16 with fp32
 // accumulation; P^ and dS are rounded to bf16 as MFMA operands.
