@@ -10,7 +10,7 @@
 //                      listed in ascending order                       (chunk_topk_kernel)
 // The summaries are the part CISA keeps between steps; they are an output.  Reading K once
 // is the whole cost (HBM-bound); the selection itself works on n_chunks scores per (b, g)
-// in LDS: a bitonic sort of (score, id) keys, then an ascending compaction.
+// in LDS: a radix select of the topk-th key, then an ascending compaction.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -68,16 +68,22 @@ __global__ void __launch_bounds__(256) chunk_summary_kernel(ChunkParams p) {
   }
 }
 
-constexpr int kMaxChunks = 8192;  // per (b, g): the sort keys fill 64 KB of LDS
+constexpr int kMaxChunks = 8192;  // per (b, g): one 32-bit key per chunk in LDS
 
-// top-k: one workgroup of 1024 threads per (b, g)
+// top-k: one workgroup of 1024 threads per (b, g).  Each chunk gets the 32-bit key
+// u = ~(order-preserving bits of its score), so ascending u is descending score, and the
+// selection is the topk smallest (u, id) pairs: a radix select finds the topk-th smallest u
+// (T) and how many chunks with u == T it takes (need); one scan in id order then writes the
+// ids with u < T, and the first `need` ids with u == T, in ascending order.
 template <int D>
 __global__ void __launch_bounds__(1024) chunk_topk_kernel(ChunkParams p) {
   __shared__ float iq[D];
-  __shared__ uint64_t keys[kMaxChunks];
-  __shared__ int flag[kMaxChunks];
-  __shared__ int cnt[1024];
+  __shared__ uint32_t uk[kMaxChunks];
+  __shared__ int hist[256];
+  __shared__ int wsum[16];
+  __shared__ int pick[2];  // digit of the pass, chunks in the bins below it
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int bg = blockIdx.x;
   const int b = bg / p.Hkv, g = bg - b * p.Hkv;
   const int n = p.n_chunks, npad = p.n_pad;
@@ -92,10 +98,8 @@ __global__ void __launch_bounds__(1024) chunk_topk_kernel(ChunkParams p) {
   __syncthreads();
   // scores, coalesced: D/4 lanes read one summary row (16 bytes each) and reduce its dot
   // product by shuffles; every wave keeps U loads (U * 64 / (D / 4) rows) in flight.
-  // key = (descending score, ascending id): ~(order-preserving score bits) << 32 | id
   {
     constexpr int LPR = D / 4, RPI = 64 / LPR, U = 8;
-    const int lane = tid & 63, wave = tid >> 6;
     const int sub = lane / LPR, e0 = (lane % LPR) * 4;
     const float q0 = iq[e0], q1 = iq[e0 + 1], q2 = iq[e0 + 2], q3 = iq[e0 + 3];
     const float* srow = p.summ + (int64_t)bg * n * D + e0;
@@ -113,104 +117,89 @@ __global__ void __launch_bounds__(1024) chunk_topk_kernel(ChunkParams p) {
 #pragma unroll
         for (int m = 1; m < LPR; m <<= 1) s[u] += __shfl_xor(s[u], m, 64);
         const int c = cb + u * RPI + sub;
-        if (lane % LPR == 0 && c < npad) {
-          uint64_t key = ~uint64_t(0);
-          if (c < n) {
-            const uint32_t w = __float_as_uint(s[u]);
-            const uint32_t ord = (w >> 31) ? ~w : (w | 0x80000000u);
-            key = (uint64_t(~ord) << 32) | uint32_t(c);
-          }
-          keys[c] = key;
+        if (lane % LPR == 0 && c < n) {
+          const uint32_t w = __float_as_uint(s[u]);
+          uk[c] = ~((w >> 31) ? ~w : (w | 0x80000000u));
         }
       }
     }
   }
   __syncthreads();
-  // bitonic sort, ascending.  Element i of the network lives in LDS, except during the stages
-  // whose partner distance j is below 64: then lane i % 64 of wave (i / 64) % 16 holds it in
-  // register i / 1024 and takes the partner's key by a lane shuffle, so those stages need no
-  // barrier (21 of the 78 stages of 4096 keys go through LDS).
-  {
-    constexpr int RMAX = kMaxChunks / 1024;
-    const int nreg = npad >= 1024 ? npad / 1024 : 1;
-    uint64_t a[RMAX];
-    auto reg_load = [&]() __attribute__((always_inline)) {
-#pragma unroll
-      for (int r = 0; r < RMAX; ++r) {
-        const int i = tid + 1024 * r;
-        if (r < nreg) a[r] = i < npad ? keys[i] : ~uint64_t(0);
-      }
-    };
-    auto reg_store = [&]() __attribute__((always_inline)) {
-#pragma unroll
-      for (int r = 0; r < RMAX; ++r) {
-        const int i = tid + 1024 * r;
-        if (r < nreg && i < npad) keys[i] = a[r];
-      }
-    };
-    // every lane of the workgroup runs the shuffles (nreg is uniform); lanes past npad hold
-    // dummies whose partners are dummies too (npad is a power of two and j < npad)
-    auto reg_stage = [&](int k, int j) __attribute__((always_inline)) {
-#pragma unroll
-      for (int r = 0; r < RMAX; ++r) {
-        if (r < nreg) {
-          const int i = tid + 1024 * r;
-          const int lo = __shfl_xor((int)(uint32_t)a[r], j, 64);
-          const int hi = __shfl_xor((int)(uint32_t)(a[r] >> 32), j, 64);
-          const uint64_t o = (uint64_t(uint32_t(hi)) << 32) | uint32_t(lo);
-          const bool up = (i & k) == 0, lower = (i & j) == 0;
-          const uint64_t mn = a[r] < o ? a[r] : o, mx = a[r] < o ? o : a[r];
-          a[r] = lower == up ? mn : mx;
-        }
-      }
-    };
-    reg_load();
-    for (int k = 2; k <= min(64, npad); k <<= 1)
-      for (int j = k >> 1; j > 0; j >>= 1) reg_stage(k, j);
-    reg_store();
+
+  // radix select, 8 bits per pass from the top: among the keys that match the digits fixed
+  // so far, the bin holding the kk-th smallest key fixes the next digit
+  uint32_t prefix = 0, mask = 0;
+  int kk = p.topk;  // rank (from 1) of the wanted key among the keys that match prefix
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    if (tid < 256) hist[tid] = 0;
     __syncthreads();
-    for (int k = 128; k <= npad; k <<= 1) {
-      for (int j = k >> 1; j >= 64; j >>= 1) {
-        for (int i = tid; i < npad; i += 1024) {
-          const int l = i ^ j;
-          if (l > i) {
-            const uint64_t x = keys[i], y = keys[l];
-            const bool up = (i & k) == 0;
-            if ((x > y) == up) {
-              keys[i] = y;
-              keys[l] = x;
-            }
-          }
-        }
-        __syncthreads();
-      }
-      reg_load();
-      for (int j = 32; j > 0; j >>= 1) reg_stage(k, j);
-      reg_store();
-      __syncthreads();
+    for (int c = tid; c < n; c += 1024) {
+      const uint32_t u = uk[c];
+      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
     }
+    __syncthreads();
+    if (wave == 0) {
+      int h[4], loc = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        h[j] = hist[4 * lane + j];
+        loc += h[j];
+      }
+      int inc = loc;  // inclusive scan over the wave's lanes
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(inc, o, 64);
+        inc += lane >= o ? v : 0;
+      }
+      int before = inc - loc;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (before < kk && kk <= before + h[j]) {  // exactly one bin of the wave
+          pick[0] = 4 * lane + j;
+          pick[1] = before;
+        }
+        before += h[j];
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)pick[0] << shift;
+    mask |= 255u << shift;
+    kk -= pick[1];
   }
-  // the first topk keys are the selection; list their ids in ascending order
-  for (int c = tid; c < n; c += 1024) flag[c] = 0;
-  __syncthreads();
-  for (int i = tid; i < p.topk; i += 1024) flag[(int)(uint32_t)keys[i]] = 1;
-  __syncthreads();
-  const int per = (n + 1023) / 1024;
+  const uint32_t T = prefix;  // the topk-th smallest key
+  const int need = kk;        // chunks with key T that are selected (1 .. count of them)
+
+  // scan in id order: thread t owns ids [t per, (t + 1) per); counts of keys below T (low
+  // 16 bits) and equal to T (high 16 bits), n <= 8192 so neither overflows
+  const int per = (n + 1023) >> 10;
   const int c0 = min(n, tid * per), c1 = min(n, c0 + per);
-  int local = 0;
-  for (int c = c0; c < c1; ++c) local += flag[c];
-  cnt[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {  // inclusive scan (Hillis-Steele)
-    const int v = tid >= off ? cnt[tid - off] : 0;
-    __syncthreads();
-    cnt[tid] += v;
-    __syncthreads();
+  int loc = 0;
+  for (int c = c0; c < c1; ++c) {
+    const uint32_t u = uk[c];
+    loc += (u < T ? 1 : 0) + (u == T ? 0x10000 : 0);
   }
-  int pos = cnt[tid] - local;
+  int inc = loc;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(inc, o, 64);
+    inc += lane >= o ? v : 0;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  int pre = inc - loc;
+  for (int w = 0; w < wave; ++w) pre += wsum[w];
+  int lt = pre & 0xffff, eq = pre >> 16;
   int32_t* out = p.chunks + (int64_t)bg * p.topk;
-  for (int c = c0; c < c1; ++c)
-    if (flag[c]) out[pos++] = c;
+  for (int c = c0; c < c1; ++c) {
+    const uint32_t u = uk[c];
+    if (u < T) {
+      out[lt + min(eq, need)] = c;
+      ++lt;
+    } else if (u == T) {
+      if (eq < need) out[lt + eq] = c;
+      ++eq;
+    }
+  }
 }
 
 hipError_t launch_chunk_select(const ChunkParams& p, hipStream_t stream) {
