@@ -48,8 +48,8 @@ def check_unit(summ_gpu, sel_gpu, q, k, chunk, topk, query_index, label):
     _say(f"{label}: summary err {err:.2e}; selection {'equal' if exact else 'equal up to near-ties'}")
 
 
-# chunk counts n: 301, 136, 16, then the sort's edge sizes -- 8192 (the maximum: eight keys
-# per thread), 1025 (padded to 2048: two per thread) and a single short chunk
+# chunk counts n: 301, 136, 16, then the selection's edge sizes -- 8192 (the maximum: eight
+# keys per thread), 1025 (two per thread for some threads) and a single short chunk
 @pytest.mark.parametrize("d,Nk,chunk,topk,Hq,Hkv", [(128, 64 * 300 + 17, 64, 120, 8, 2), (64, 5000, 37, 50, 4, 4),
                                                  (128, 1024, 64, 16, 2, 1), (128, 8 * 8192, 8, 3000, 4, 2),
                                                  (64, 16 * 1025, 16, 1000, 2, 1), (128, 20, 64, 1, 2, 2)])
@@ -67,6 +67,37 @@ def test_chunk_select_small(d, Nk, chunk, topk, Hq, Hkv):
         for g in range(Hkv):
             check_unit(summ[b, g], chunks[b, g], q[b:b + 1, :, g * grp:(g + 1) * grp], k[b:b + 1, :, g:g + 1],
                        chunk, topk, Nq - 1, f"b{b} g{g}")
+
+
+def test_chunk_select_every_chunk():
+    # topk = n: every chunk is selected, in ascending order
+    rng = np.random.default_rng(11)
+    q = normal_bf16(rng, (1, 9, 2, 128))
+    k = normal_bf16(rng, (1, 64 * 100 - 5, 1, 128))
+    _, chunks = bs.chunk_select(_dev(q), _dev(k), 1, 64, 100)
+    torch.cuda.synchronize()
+    assert np.array_equal(chunks.cpu().numpy()[0, 0], np.arange(100))
+
+
+@pytest.mark.parametrize("topk", [1, 150, 300, 467, 699])
+def test_chunk_select_exact_ties(topk):
+    # chunk c holds key pattern c % 3: three exactly tied score levels (identical chunks
+    # give bitwise identical float32 and float64 scores), so the selection at the cut must
+    # take the lowest ids of the tied level, exactly as the oracle does
+    rng = np.random.default_rng(12)
+    chunk, n, d = 16, 700, 128
+    pats = normal_bf16(rng, (3, chunk, d))
+    k = np.concatenate([pats[c % 3] for c in range(n)], axis=0)[None, :, None, :]
+    q = normal_bf16(rng, (1, 5, 4, d))
+    summ, chunks = bs.chunk_select(_dev(q), _dev(k), 1, chunk, topk)
+    torch.cuda.synchronize()
+    sel = chunks.cpu().numpy()[0, 0]
+    summ_ref, iq = chunk_summaries(k, chunk)[0, 0], indexing_queries(q, 1, 4)[0, 0]
+    s = np.array([summ_ref[c] @ iq for c in range(n)])  # one dot per chunk: tied chunks tie exactly
+    assert len(np.unique(s)) == 3
+    ref = select_chunks(s[None, None], topk)[0, 0]
+    _say(f"ties topk={topk}: selected {len(sel)}, first {sel[:4]}")
+    assert np.array_equal(sel, ref)
 
 
 def test_chunk_select_long_prefill_sampled():
