@@ -664,9 +664,6 @@ __device__ __forceinline__ void pp_walk(const FwdParams& p, const CONST_AS int32
     constexpr int n1 = QK ? kNPV + kNQK : kNPV;
     constexpr int kSpread = (n1 - n0) / C::kInst;  // one load before every kSpread-th product
     static_assert(kSpread >= 1, "a product per load");
-    // ... starting two products into the phase: the first load then no longer queues behind
-    // the page loads the other group's waves issued at the start of their vector phase
-    constexpr int kOff = 2 % kSpread;
     if constexpr (!ACT) {
       if (ldk) {
 #pragma unroll
@@ -719,7 +716,7 @@ __device__ __forceinline__ void pp_walk(const FwdParams& p, const CONST_AS int32
     static_for<n0, (n0 + kLead < n1 ? n0 + kLead : n1)>(load);
     static_for<n0, n1>([&](auto it) __attribute__((always_inline)) {
       constexpr int i = decltype(it)::value;
-      if constexpr ((i - n0) % kSpread == kOff) {
+      if constexpr ((i - n0) % kSpread == 0) {
         constexpr int tt = (i - n0) / kSpread;
         if constexpr (tt < C::kInst) {
           if (ldk) fire(*ldk, krsrc, kdst, tt);
@@ -735,7 +732,7 @@ __device__ __forceinline__ void pp_walk(const FwdParams& p, const CONST_AS int32
     });
     static_for<n0, n1>([&](auto it) __attribute__((always_inline)) {
       constexpr int i = decltype(it)::value;
-      if constexpr ((i - n0) % kSpread == kOff && (i - n0) / kSpread < C::kInst) {
+      if constexpr ((i - n0) % kSpread == 0 && (i - n0) / kSpread < C::kInst) {
         if (ldk) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
       if constexpr (i + kLead < n1) __builtin_amdgcn_sched_group_barrier(0x100, i + kLead < kNPV ? 2 : 1, 0);
