@@ -67,7 +67,6 @@ struct BwdParams {
   int64_t o_sb, o_sn, o_sh;
   const QTileDev* dq_tiles;   // 128-row Q tiles (row0, rows, qblock): the last n_dq_split
                               // hold at most kDqSplitRows rows
-
   const QTileDev* kv_tiles;   // 64-row K tiles (first slot, rows, kblock)
   const int32_t* pl_ptr;      // K pages per (unit, Q block), as in the forward
   const int32_t* pl_ent;
