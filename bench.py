@@ -40,6 +40,7 @@ SHORT_NAMES = {1: "tiny3d", 2: "onedim", 3: "videodit3d", 4: "partitions", 5: "c
 KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_fwd_amd", "csrc", "fwd_kernel.hip")
 DECODE_SRC = os.path.join(ROOT, "block_sparse_attention_fwd_amd", "csrc", "decode_kernel.hip")
 CHUNK_SRC = os.path.join(ROOT, "block_sparse_attention_fwd_amd", "csrc", "chunk_select.hip")
+BWD_SRC = os.path.join(ROOT, "block_sparse_attention_fwd_amd", "csrc", "bwd_kernel.hip")
 
 
 def measured_counters(workload, name=None, src=KERNEL_SRC):
@@ -215,7 +216,11 @@ def bench_bwd(args, w, plan, st, t_plan, dev):
                    "Nk": w.Nk, "d": w.d, "useful_pairs": st["useful"],
                    "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2), "plan_ms": round(t_plan * 1e3, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     # HBM bytes of one backward call (all its kernels) from the committed counter runs
+                     "traffic": measured_bytes(f"bwd_{SHORT_NAMES.get(args.workload, '')}", BWD_SRC,
+                                               ("bwd_dot_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel",
+                                                "bwd_dq_kernel_split")),
                      "kernel": f"bsattn_bwd: bwd_dot + bwd_dkdv<{w.d}> + bwd_dq<{w.d}>", "kernel_ms": round(ev_ms, 4)},
         "cpu_baseline": cpu,
     }
